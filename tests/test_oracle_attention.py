@@ -1,0 +1,129 @@
+"""Pins of the oracle's corrected chunk attention and attention masses (abstract; §1, Fig. 2)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_kv_cache_kvq_amd import synth
+from oracle.attention import attend_head
+from oracle.correction import bias_taylor_per_token
+from oracle.quant import Format, bf16_to_f32
+
+
+def _brute(q, kc, vc, kr, vr, s, bias):
+    nq, d = q.shape
+    O = np.zeros((nq, vr.shape[1]))
+    PS = np.zeros(nq)
+    for i in range(nq):
+        logits = [s * sum(q[i, c] * kc[j, c] for c in range(d)) - bias[i, j] for j in range(len(kc))]
+        logits += [s * sum(q[i, c] * kr[r, c] for c in range(d)) for r in range(len(kr))]
+        m = max(logits)
+        e = [math.exp(v - m) for v in logits]
+        z = sum(e)
+        vals = list(vc) + list(vr)
+        for t, et in enumerate(e):
+            O[i] += et * vals[t] / z
+        PS[i] = sum(e[: len(kc)]) / z
+    return O, PS
+
+
+def test_blocked_attention_matches_brute_force():
+    rng = np.random.default_rng(20)
+    nq, nc, nr, d = 7, 11, 5, 8
+    q, kc, vc = rng.standard_normal((nq, d)), rng.standard_normal((nc, d)), rng.standard_normal((nc, d))
+    kr, vr = rng.standard_normal((nr, d)), rng.standard_normal((nr, d))
+    bias = rng.uniform(0, 0.5, (nq, nc))
+    s = 0.35
+    O, PS, PR = attend_head(q, kc, vc, kr, vr, s, lambda rows: bias[rows], block=3)
+    Ob, PSb = _brute(q, kc, vc, kr, vr, s, bias)
+    np.testing.assert_allclose(O, Ob, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(PS, PSb, rtol=1e-12)
+    np.testing.assert_allclose(PS + PR, 1, rtol=1e-14)
+
+
+def test_matches_library_sdpa_with_bias_mask():
+    # corrected attention == softmax attention with an additive mask of -b on cached columns
+    rng = np.random.default_rng(21)
+    nq, nc, nr, d = 33, 70, 40, 64
+    q, kc, vc = rng.standard_normal((nq, d)), rng.standard_normal((nc, d)), rng.standard_normal((nc, d))
+    kr, vr = rng.standard_normal((nr, d)), rng.standard_normal((nr, d))
+    dl = rng.uniform(0.2, 1.2, nc)
+    s = 1 / np.sqrt(d)
+    bias = bias_taylor_per_token(q, dl, s)
+    O, PS, PR = attend_head(q, kc, vc, kr, vr, s, lambda rows: bias[rows], block=16)
+    mask = np.concatenate([-bias, np.zeros((nq, nr))], axis=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None], torch.tensor(np.concatenate([kc, kr]))[None],
+        torch.tensor(np.concatenate([vc, vr]))[None], attn_mask=torch.tensor(mask)[None], scale=s)[0].numpy()
+    np.testing.assert_allclose(O, ref, rtol=1e-10, atol=1e-12)
+    ref0 = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None], torch.tensor(np.concatenate([kc, kr]))[None],
+        torch.tensor(np.concatenate([vc, vr]))[None], scale=s)[0].numpy()
+    O0, _, _ = attend_head(q, kc, vc, kr, vr, s, None, block=16)
+    np.testing.assert_allclose(O0, ref0, rtol=1e-10, atol=1e-12)
+
+
+def test_zero_step_means_no_correction():
+    # a constant cached key quantizes with Delta = 0, so its correction vanishes (Delta=0 -> b=0)
+    w = synth.WORKLOADS["tiny"]
+    x = synth.draw_all(w)
+    kc = x["k_cache"].copy()
+    kc[:, :, 5, :] = synth.f32_to_bf16_bits(np.full(w.d, 0.5, dtype=np.float32))
+    kf, vf = Format(2, "token", 128, False, "key"), Format(2, "token", 128, False, "value")
+    args = (x["q"], kc, x["v_cache"], x["k_cur"], x["v_cur"])
+    Ot, _, _, cache = oracle.reference_call(*args, chunk_len=w.chunk_len, k_fmt=kf, v_fmt=vf, correction="taylor")
+    assert cache["k_scale"][0, 0, 5] == 0
+    np.testing.assert_allclose(cache["k_hat"][0, 0, 5], 0.0)
+
+
+def test_quantized_equals_unquantized_when_exact():
+    # values already on an INT4 grid with an exact step reproduce the BF16 reference exactly
+    w = synth.WORKLOADS["tiny"].replace(chunk_len=64, n_chunks=2, n_q=64)
+    rng = np.random.default_rng(22)
+    grid = rng.integers(0, 16, size=(1, 2, w.n_c, w.d)).astype(np.float32) * np.float32(0.25)
+    grid[..., 0] = 0.0
+    grid[..., 1] = 3.75
+    kc = synth.f32_to_bf16_bits(grid)
+    x = synth.draw_all(w)
+    kf, vf = Format(4, "token", 128, False, "key"), Format(4, "token", 128, False, "value")
+    args = (x["q"], kc, kc, x["k_cur"], x["v_cur"])
+    Oq, PSq, _, _ = oracle.reference_call(*args, chunk_len=w.chunk_len, k_fmt=kf, v_fmt=vf, correction="none")
+    Ob, PSb, _, _ = oracle.reference_call(*args, chunk_len=w.chunk_len, k_fmt=kf, v_fmt=vf, quantized=False)
+    np.testing.assert_allclose(Oq, Ob, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(PSq, PSb, rtol=1e-12)
+
+
+def _mass_stat(name, nrows, head=(0, 0), hadamard=True):
+    w = synth.WORKLOADS[name]
+    x = synth.draw_all(w, heads=[head])
+    x = {k: v[None] for k, v in x.items()}
+    kf = Format(w.bits, w.k_granularity, w.group, hadamard, "key")
+    vf = Format(w.bits, "token", w.group, hadamard, "value")
+    rows = np.arange(min(nrows, w.n_q))
+    args = (x["q"], x["k_cache"], x["v_cache"], x["k_cur"], x["v_cur"])
+    kw = dict(chunk_len=w.chunk_len, k_fmt=kf, v_fmt=vf, rows=rows)
+    _, ps_b, _, _ = oracle.reference_call(*args, quantized=False, **kw)
+    _, ps_u, _, cache = oracle.reference_call(*args, correction="none", **kw)
+    _, ps_c, _, _ = oracle.reference_call(*args, correction="taylor", cache=cache, **kw)
+    unc = np.abs(ps_u - ps_b).mean()
+    cor = np.abs(ps_c - ps_b).mean()
+    improved = np.mean(np.abs(ps_c - ps_b) < np.abs(ps_u - ps_b))
+    return unc, cor, improved, (ps_u - ps_b).mean()
+
+
+@pytest.mark.parametrize("name,nrows", [("tiny", 128), ("c24", 256), ("c40", 128)])
+def test_correction_restores_attention_mass(name, nrows):
+    # Fig. 2 / abstract: quantized keys steal mass from the current chunk (P_S rises);
+    # the correction moves P_S back toward its BF16 value.
+    unc, cor, improved, shift = _mass_stat(name, nrows)
+    assert shift > 0, "INT2 keys should inflate the cached-block mass"
+    assert cor < unc
+    assert improved > 0.6
+
+
+@pytest.mark.slow
+def test_correction_restores_attention_mass_long_window():
+    unc, cor, improved, shift = _mass_stat("long", 64)
+    assert shift > 0 and cor < unc and improved > 0.6

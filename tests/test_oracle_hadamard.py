@@ -1,0 +1,105 @@
+"""Pins of the oracle's Hadamard rotation (paper §3 "Hadamard rotation")."""
+import numpy as np
+import pytest
+
+from oracle.hadamard import fwht_f32, rotate_f64, scale_f32, sylvester
+from tests.conftest import golden_lines
+
+
+def test_sylvester_matches_written_out_matrix():
+    rows = [list(map(float, ln.split())) for ln in golden_lines("hadamard_8.txt")]
+    h8 = np.array(rows)
+    assert h8.shape == (8, 8)
+    np.testing.assert_array_equal(sylvester(8) * np.sqrt(8), h8)
+
+
+@pytest.mark.parametrize("d", [2, 4, 8, 16, 32, 64, 128, 256])
+def test_orthonormal_symmetric_involution(d):
+    h = sylvester(d)
+    np.testing.assert_allclose(h @ h.T, np.eye(d), atol=1e-14)
+    np.testing.assert_array_equal(h, h.T)
+    np.testing.assert_allclose(h @ h, np.eye(d), atol=1e-14)
+    # entries are +-1/sqrt(d) with the popcount sign pattern
+    i, j = np.meshgrid(np.arange(d), np.arange(d), indexing="ij")
+    par = np.vectorize(lambda a: bin(a).count("1") & 1)(i & j)
+    np.testing.assert_array_equal(np.sign(h), np.where(par, -1.0, 1.0))
+
+
+def test_fwht_worked_examples():
+    for ln in golden_lines("fwht_worked.txt"):
+        xs, ys = ln.split("|")
+        x = np.array(xs.split(), dtype=np.float32)
+        y = np.array(ys.split(), dtype=np.float32)
+        np.testing.assert_array_equal(fwht_f32(x), y)
+        np.testing.assert_allclose(rotate_f64(x), y, atol=1e-14)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwht_f32_equals_matrix_within_rounding(d):
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((4096, d)) * np.where(np.arange(d) < 4, 10.0, 1.0)).astype(np.float32)
+    y = fwht_f32(x).astype(np.float64)
+    ref = x.astype(np.float64) @ sylvester(d)
+    u = 2.0 ** -24
+    bound = (np.log2(d) + 2) * u * np.abs(x).astype(np.float64).sum(axis=1, keepdims=True) / np.sqrt(d)
+    assert np.all(np.abs(y - ref) <= bound)
+    # the order is fixed: a second evaluation is bit-identical
+    np.testing.assert_array_equal(fwht_f32(x), fwht_f32(x))
+
+
+def test_scale_constants():
+    assert scale_f32(64) == np.float32(0.125)
+    assert scale_f32(128) == np.float32(1.0 / np.sqrt(128.0))
+    assert abs(float(scale_f32(128)) - 0.08838834764831845) < 1e-8
+
+
+def test_rotation_preserves_scores():
+    # (Hq).(Hk) = q.k: the rotation leaves every attention score unchanged (§3)
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((64, 128))
+    k = rng.standard_normal((96, 128))
+    k[:, :4] *= 10
+    np.testing.assert_allclose(rotate_f64(q) @ rotate_f64(k).T, q @ k.T, rtol=1e-12, atol=1e-11)
+
+
+def test_rotation_spreads_outliers():
+    # an outlier channel's energy is spread over all channels (§3): max |y| shrinks
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((1000, 128))
+    k[:, :4] *= 10
+    y = rotate_f64(k)
+    assert np.abs(y).max(axis=1).mean() < 0.5 * np.abs(k).max(axis=1).mean()
+    np.testing.assert_allclose((y ** 2).sum(1), (k ** 2).sum(1), rtol=1e-12)
+
+
+def _fwht_loop(x):
+    """The butterfly order written as plain loops (stage h = 1, 2, ..., d/2; pair i, i+h)."""
+    y = [np.float32(v) for v in x]
+    d = len(y)
+    h = 1
+    while h < d:
+        for i in range(d):
+            if i & h == 0:
+                a, b = y[i], y[i + h]
+                y[i], y[i + h] = np.float32(a + b), np.float32(a - b)
+        h *= 2
+    return np.array([np.float32(v * scale_f32(d)) for v in y], dtype=np.float32)
+
+
+@pytest.mark.parametrize("d", [8, 64, 128])
+def test_fwht_f32_follows_stated_order_bit_exactly(d):
+    rng = np.random.default_rng(30 + d)
+    for _ in range(20):
+        x = (rng.standard_normal(d) * rng.uniform(0.1, 100)).astype(np.float32)
+        np.testing.assert_array_equal(fwht_f32(x), _fwht_loop(x))
+    # the order matters in float32: reversing the stages changes some results
+    x = (rng.standard_normal((2000, d)) * 7).astype(np.float32)
+    rev = np.array(x, copy=True)
+    h = d // 2
+    while h >= 1:
+        v = rev.reshape(-1, d // (2 * h), 2, h)
+        a, b = v[:, :, 0, :].copy(), v[:, :, 1, :].copy()
+        v[:, :, 0, :], v[:, :, 1, :] = a + b, a - b
+        rev = v.reshape(-1, d)
+        h //= 2
+    assert np.any(rev * scale_f32(d) != fwht_f32(x))

@@ -91,3 +91,31 @@ def test_monte_carlo_jensen_gap(d):
     rem = (x ** 4 / 180).sum()
     assert -4 * se / mean <= bt - gap <= rem + 4 * se / mean
     assert gap > 0
+
+
+def test_per_channel_bias_uses_rotated_query_monte_carlo():
+    # Per-channel steps live in the rotated basis: the stored-basis error eps (uniform per
+    # channel) perturbs the un-rotated key by H eps, so the score noise is s q.(H eps) =
+    # s (Hq).eps. Sample that directly and compare with the oracle's bias for rotated
+    # per-channel keys, which must use the rotated query.
+    from oracle.attention import _bias_fn
+    from oracle.hadamard import sylvester
+    from oracle.quant import Format
+    rng = np.random.default_rng(40)
+    d, group = 16, 64
+    H = sylvester(d)
+    q = rng.standard_normal((1, d)) * 2
+    delta = np.zeros((1, 1, 1, d), dtype=np.float16)
+    delta[0, 0, 0] = rng.uniform(0.05, 1.5, d).astype(np.float16)
+    cache = {"k_scale": delta, "n_chunks": 1}
+    fmt = Format(2, "channel", group, True, "key")
+    s = 1 / np.sqrt(d)
+    b = _bias_fn(q, cache, 0, 0, group, fmt, s, "exact")(np.array([0]))[0, 0]
+    dl = delta[0, 0, 0].astype(np.float64)
+    n = 1_000_000
+    eps = (rng.random((n, d)) - 0.5) * dl
+    e = np.exp(s * (eps @ H) @ q[0])
+    mean, se = e.mean(), e.std() / np.sqrt(n)
+    assert abs(np.log(mean) - b) <= 4 * se / mean
+    b_unrot = bias_exact(q, dl[None, :], s)[0, 0]
+    assert abs(np.log(mean) - b_unrot) > 8 * se / mean   # the rotation matters for this q

@@ -1,0 +1,210 @@
+"""Benchmark: Jensen-bias-corrected INT2 chunk attention on one MI355X.
+
+One step = the whole hot path for one chunk of the c40 workload (B=1, H=40, d=128,
+current chunk 4680 tokens, window of 8 cached chunks = 37,440 tokens, per-token INT2
+keys and values with Hadamard rotation, Taylor correction):
+  1. jb_attn_fwd: corrected attention of the chunk's queries over [window ; chunk],
+     with the cached/current masses;
+  2. kvq_pack of the chunk's keys and values (what the cache stores for the next chunk).
+Inputs are resident in HBM before timing starts. ``value`` is attention TFLOP/s over the
+step time, counting the algorithmic FLOP 4 * n_q * (n_c + n_r) * d * B * H (QK^T + PV).
+
+Printed: one JSON line with the driver's fields plus ``roofline`` (the attention kernel,
+timed with HIP events on the stream it runs on, against the 2.5 PFLOP/s dense fp16/bf16
+MFMA peak) and ``cpu_baseline`` (the float64 oracle on a bounded sample, on host cores).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "jb_attn TFLOP/s + cache GB/s (% roofline), INT2 corrected, 40H d128 chunk 4680"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "jb_attn_c40_counters.md")
+KERNEL_SOURCE = os.path.join(ROOT, "bit_kv_cache_kvq_amd", "csrc", "attn.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from the committed counter summary, if it describes this kernel."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", txt)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, x, heads, kf_o, vf_o):
+    """Time the oracle (as it stands) on `heads`: pack of the current chunk + attention."""
+    import numpy as np
+    import oracle
+    from oracle.quant import pack_window
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    xs = {k: np.stack([v[b, h] for (b, h) in heads])[None] for k, v in x.items()}
+    cache = oracle.attention.quantize_cache(xs["k_cache"], xs["v_cache"], w.chunk_len, kf_o, vf_o)
+    t0 = time.perf_counter()
+    pack_window(xs["k_cur"], w.n_r, kf_o)
+    pack_window(xs["v_cur"], w.n_r, vf_o)
+    O, PS, PR, _ = oracle.reference_call(xs["q"], xs["k_cache"], xs["v_cache"], xs["k_cur"], xs["v_cur"],
+                                         chunk_len=w.chunk_len, k_fmt=kf_o, v_fmt=vf_o, correction="taylor",
+                                         cache=cache)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.n_q * (w.n_c + w.n_r) * w.d * len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(heads)} of {w.bh} heads, all {w.n_q} query rows: float64 attention over the "
+                      f"dequantized window + current chunk, plus float32-contract packing of the current "
+                      f"chunk's K and V ({dt:.1f} s)"}, (O, PS, PR)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c40")
+    ap.add_argument("--bits", type=int, default=None)
+    ap.add_argument("--correction", type=int, default=1)
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle timing sample (0: skip)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="only run a device copy of this many MiB (HBM counter calibration) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the path shards by head with no communication; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_kv_cache_kvq_amd import kvq, synth
+    from oracle.quant import Format
+
+    torch.cuda.set_device(0)
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4, "launches": 5}))
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    if args.bits:
+        w = w.replace(bits=args.bits)
+    t_gen = time.perf_counter()
+    x = synth.draw_all(w)
+    print(f"# generated {w.name} inputs in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    kf = kvq.KvqFormat.make(w.bits, w.k_granularity, w.group, True, "key")
+    vf = kvq.KvqFormat.make(w.bits, "token", w.group, True, "value")
+    q, kr, vr = dev(x["q"]), dev(x["k_cur"]), dev(x["v_cur"])
+    kwin = kvq.pack_window(dev(x["k_cache"]), w.chunk_len, kf)
+    vwin = kvq.pack_window(dev(x["v_cache"]), w.chunk_len, vf)
+    o = torch.empty((w.B, w.H, w.n_q, w.d), dtype=torch.float32, device="cuda")
+    ms = torch.empty((w.B, w.H, w.n_q), dtype=torch.float32, device="cuda")
+    mr = torch.empty_like(ms)
+    knext = kvq.alloc_window(kf, w.B, w.H, w.d, w.n_r, 1)
+    vnext = kvq.alloc_window(vf, w.B, w.H, w.d, w.n_r, 1)
+    a = kvq.make_args(q, kr, vr, kwin, vwin, w.chunk_len, w.n_chunks, kf, vf, o=o, mass_s=ms, mass_r=mr,
+                      correction=args.correction)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kvq.jb_attn_fwd(a, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        kvq.kvq_pack(kr, kf, 1, 0, *knext, stream)
+        kvq.kvq_pack(vr, vf, 1, 0, *vnext, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = float(np.mean([e0.elapsed_time(e1) for (e0, e1) in evs]))
+
+    flops = w.flops()
+    cache_bytes = (kwin[0].numel() * 4 + kwin[1].numel() * 2 * 2 + vwin[0].numel() * 4 + vwin[1].numel() * 2 * 2)
+    # algorithmic bytes of one attention call: the cache window once, Q/K_r/V_r (bf16), O and masses (fp32)
+    algo_bytes = cache_bytes + 3 * w.bh * w.n_q * w.d * 2 + w.bh * w.n_q * (w.d + 2) * 4
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    traffic = traffic_from_profile()
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} d={w.d}, current chunk {w.n_q} tokens, window "
+                               f"{w.n_chunks}x{w.chunk_len} cached tokens, INT{w.bits} per-{w.k_granularity} K, "
+                               f"per-token V, Hadamard, correction={'taylor' if args.correction else 'none'}",
+                   "B": w.B, "H": w.H, "d": w.d, "n_q": w.n_q, "n_c": w.n_c, "bits": w.bits,
+                   "parallelism": "none (1 GPU)"},
+        "attn_ms": round(attn_ms, 4),
+        "cache_GBps": round(cache_bytes / (attn_ms * 1e-3) / 1e9, 2),
+        "cache_frac_hbm": round(cache_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": (round(traffic) if traffic is not None else None),
+                     "algorithmic_bytes": algo_bytes, "kernel_source_sha256_16": kernel_source_hash()},
+    }
+    if args.cpu_heads > 0:
+        heads = [(0, h) for h in range(min(args.cpu_heads, w.bh))] if w.B == 1 else \
+            [(b, h) for b in range(w.B) for h in range(w.H)][: args.cpu_heads]
+        kf_o = Format(w.bits, w.k_granularity, w.group, True, "key")
+        vf_o = Format(w.bits, "token", w.group, True, "value")
+        base, (O, PS, PR) = cpu_baseline(w, x, heads, kf_o, vf_o)
+        og = np.stack([o[b, h].cpu().numpy() for (b, h) in heads])[None]
+        rms = np.sqrt((O ** 2).mean())
+        err = np.abs(og - O)
+        rec["cpu_baseline"] = base
+        rec["parity_on_sample"] = {"max_err_over_rms": float(err.max() / rms), "mean_err_over_rms": float(err.mean() / rms)}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

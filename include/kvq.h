@@ -1,0 +1,160 @@
+/* kvq.h -- C ABI of libkvq: Jensen-bias-corrected chunk attention over an INT2/INT4
+ * quantized KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "Quantized Keys Steal Attention: Bias Correction for KV-Cache
+ * Compression in Video Diffusion" (Tuncer, Becker, Pfeil; arXiv 2605.26266):
+ *   - kvq_pack: the cache compression of §3 -- Hadamard rotation ("Hadamard rotation"),
+ *     asymmetric round-to-nearest integer quantization (Eq. (1)) per token or, for keys,
+ *     per channel over a group of tokens ("Quantization granularity");
+ *   - jb_attn_fwd: chunk-wise attention of the current chunk's queries over the cached
+ *     window and the unquantized current chunk (abstract; §1), with the per-score
+ *     correction b subtracted from cached-key scores before the softmax (abstract; Fig. 3
+ *     caption), computed on the fly from the cached keys' step sizes and the query, with
+ *     no extra memory; optionally the cached/current attention masses P_S, P_R (Fig. 2);
+ *   - jb_attn_mass: the masses alone.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees or keeps them. Layouts are dense row-major; every pointer must be
+ *     16-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream) and is asynchronous to the host.
+ *   - Arguments are validated on the host first. On a negative status nothing was
+ *     launched and no output was written. KVQ_ERR_HIP reports a failed launch.
+ *   - No global mutable state: calls are reentrant; calls on different streams may run
+ *     concurrently if their outputs do not overlap.
+ *   - Preconditions that are NOT checked: inputs are finite; inputs and outputs do not
+ *     alias; per group, (max - min)/(2^bits - 1) fits in fp16 (< 65504).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = -1,        /* a required pointer is NULL */
+  KVQ_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  KVQ_ERR_UNSUPPORTED = -3, /* a format/option combination this library does not implement */
+  KVQ_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  KVQ_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  KVQ_ERR_HIP = -6          /* the HIP launch failed */
+};
+
+enum { KVQ_PER_TOKEN = 0, KVQ_PER_CHANNEL = 1 };
+enum { KVQ_ROLE_KEY = 0, KVQ_ROLE_VALUE = 1 };
+enum { JB_CORR_NONE = 0, JB_CORR_TAYLOR = 1 };
+
+/* Storage format of one cached tensor.
+ *
+ * Window geometry: a window holds n_chunks chunks of chunk_len tokens. Each chunk's
+ * token axis is padded to chunk_pad = kvq_chunk_pad(chunk_len) (a multiple of 64);
+ * pad tokens hold code 0 and, per token, scale = zero = 0.
+ *
+ * Codes (c = 32/bits codes per 32-bit word):
+ *   KVQ_ROLE_KEY   uint32 [B, H, n_chunks*chunk_pad, d/c]: token-major; channel c*w + i of
+ *                  a token is in bits [bits*i, bits*i + bits) of its word w.
+ *   KVQ_ROLE_VALUE uint32 [B, H, n_chunks*chunk_pad/64, d, 64/c]: 64-token blocks, channel-
+ *                  major inside a block; word u of channel ch holds tokens c*u .. c*u+c-1 of
+ *                  the block, token c*u + i in bits [bits*i, bits*i + bits).
+ * Step size and zero point (fp16 bit patterns):
+ *   KVQ_PER_TOKEN   [B, H, n_chunks*chunk_pad]
+ *   KVQ_PER_CHANNEL [B, H, n_chunks*ceil(chunk_len/group), d]; groups restart at each
+ *                   chunk's first token, the last group of a chunk may be short.
+ *
+ * Quantizer (paper §3, Eq. (1)), one fixed float32 operation order, so results are
+ * reproducible bit for bit: y = H x in float32 (butterfly stages h = 1, 2, ..., d/2,
+ * pair (i, i+h) -> (a+b, a-b), then one multiply by float32(1/sqrt(d))) when hadamard
+ * is set, else y = x; per group mn = min y, mx = max y; d32 = (mx - mn)/(2^bits - 1)
+ * (correctly rounded); Delta = fp16(d32) (nearest even); if Delta == 0 then scale =
+ * zero = +0 and codes 0; else z = rint(-mn/Delta) + 0 (half-even, -0 -> +0, not
+ * clamped); code = clamp(rint(y/Delta) + z, 0, 2^bits - 1); scale = Delta, zero = fp16(z)
+ * (exact for |z| <= 2048). Reconstruction: x_hat' = (code - zero) * scale, x_hat = H x_hat'. */
+typedef struct {
+  int32_t bits;        /* 2 or 4 */
+  int32_t granularity; /* KVQ_PER_TOKEN, or KVQ_PER_CHANNEL (role KEY only) */
+  int32_t group;       /* tokens per channel group: 64 or 128 (KVQ_PER_CHANNEL only) */
+  int32_t hadamard;    /* 1: rotate by the normalized Sylvester-Hadamard matrix first */
+  int32_t role;        /* KVQ_ROLE_KEY or KVQ_ROLE_VALUE: selects the code layout */
+} kvq_format;
+
+/* Tokens per chunk after padding to a multiple of 64. */
+int32_t kvq_chunk_pad(int32_t chunk_len);
+
+/* Element counts of a window's arrays: *code_words (uint32) and *param_elems (fp16,
+ * for scale and for zero each). Returns KVQ_OK or a negative status for a bad format. */
+int kvq_window_elems(const kvq_format* fmt, int32_t B, int32_t H, int32_t d, int32_t chunk_len,
+                     int32_t n_chunks, size_t* code_words, size_t* param_elems);
+
+/* Quantize ONE chunk (paper §3: Hadamard rotation, Eq. (1), quantization granularity)
+ * and write it as chunk `chunk_idx` of a window of `n_chunks` chunks of n tokens.
+ *   x      bf16 [B, H, n, d], d in {64, 128}, n >= 1 (the chunk; chunk_len = n)
+ *   codes, scale, zero  the window arrays described at kvq_format; only chunk
+ *          chunk_idx's slice (its padded tokens, or its channel groups) is written.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (B,H,n < 1; d not 64/128; chunk_idx outside
+ * [0, n_chunks)), KVQ_ERR_UNSUPPORTED (bits, granularity/role/group combination),
+ * KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
+int kvq_pack(const uint16_t* x, int32_t B, int32_t H, int32_t n, int32_t d, const kvq_format* fmt,
+             int32_t n_chunks, int32_t chunk_idx, uint32_t* codes, uint16_t* scale, uint16_t* zero,
+             void* stream);
+
+/* Arguments of one attention call (abstract; §1; Fig. 2 and Fig. 3 captions).
+ * Query i of the current chunk attends, with no mask, to every valid cached token j of
+ * the window and every current-chunk token r:
+ *   l_ij = s * q_i . k_hat_j - b_ij     b_ij = s^2 * sum_c q'_ic^2 Delta_jc^2 / 24
+ *   l_ir = s * q_i . k_r                (current chunk: not quantized, no correction)
+ *   O_i  = (sum_j e^l_ij v_hat_j + sum_r e^l_ir v_r) / sum e^l
+ *   P_S,i = sum_j e^l_ij / sum e^l,  P_R,i = sum_r e^l_ir / sum e^l
+ * where q' = H q if the keys were rotated (else q), Delta_jc is the key's step size
+ * (per token: the same for every c, giving b_ij = s^2 |q_i|^2 Delta_j^2 / 24), and
+ * b is the second-order Taylor form of the expected inflation of e^l under uniform
+ * rounding noise on the cached keys. b_ij = 0 when correction == JB_CORR_NONE. */
+typedef struct {
+  int32_t B, H, d;            /* d in {64, 128}; the same H for queries and keys */
+  int32_t n_q;                /* current-chunk queries, >= 1 */
+  int32_t n_r;                /* current-chunk keys/values, >= 0 */
+  int32_t chunk_len;          /* tokens per cached chunk, >= 1 */
+  int32_t n_chunks;           /* cached chunks in the window, >= 0 */
+  const uint16_t* q;          /* bf16 [B, H, n_q, d], not rotated */
+  const uint16_t* k_cur;      /* bf16 [B, H, n_r, d] */
+  const uint16_t* v_cur;      /* bf16 [B, H, n_r, d] */
+  const uint32_t* k_codes;    /* window layout of k_fmt (role KEY) */
+  const uint16_t* k_scale;
+  const uint16_t* k_zero;
+  const uint32_t* v_codes;    /* window layout of v_fmt (role VALUE, per token) */
+  const uint16_t* v_scale;
+  const uint16_t* v_zero;
+  kvq_format k_fmt, v_fmt;    /* same bits; k: KEY per token or per channel; v: VALUE per token */
+  float softmax_scale;        /* s; 0 selects 1/sqrt(d) */
+  int32_t correction;         /* JB_CORR_NONE or JB_CORR_TAYLOR */
+  float* o;                   /* fp32 [B, H, n_q, d]: required by fwd, ignored by mass */
+  float* mass_s;              /* fp32 [B, H, n_q]: optional in fwd (NULL), required in mass */
+  float* mass_r;              /* fp32 [B, H, n_q]: as mass_s */
+  void* workspace;            /* reserved for split-window partials; may be NULL */
+  size_t workspace_bytes;
+} jb_attn_args;
+
+/* Corrected attention forward: writes o and, if given, mass_s/mass_r.
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED (mixed bits, value per-channel,
+ * wrong roles, group not 64/128), KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
+int jb_attn_fwd(const jb_attn_args* a, void* stream);
+
+/* Attention masses only (Fig. 2): writes mass_s and mass_r; o and values are not read. */
+int jb_attn_mass(const jb_attn_args* a, void* stream);
+
+/* Workspace bytes the call would use (0: none needed). */
+size_t jb_attn_workspace_bytes(const jb_attn_args* a);
+
+/* Static description of a status code. */
+const char* kvq_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

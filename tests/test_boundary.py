@@ -1,0 +1,112 @@
+"""The C ABI: libkvq.so loads, exports every function include/kvq.h declares, and its
+host-side validation rejects bad arguments before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    from bit_kv_cache_kvq_amd import kvq as mod
+    return mod
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for fn in ["kvq_pack", "jb_attn_fwd", "jb_attn_mass", "jb_attn_workspace_bytes", "kvq_status_str",
+               "kvq_chunk_pad", "kvq_window_elems"]:
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(kvq):
+    lib = ctypes.CDLL(kvq.library_path)
+    for fn in _declared_functions():
+        assert hasattr(lib, fn), fn
+    assert set(_declared_functions()) <= set(kvq.EXPORTS)
+
+
+def test_struct_layouts_match_header(kvq):
+    # five int32 fields; the attention struct has no hidden padding surprises on x86-64
+    assert ctypes.sizeof(kvq.KvqFormat) == 20
+    off = kvq.JbAttnArgs.q.offset
+    assert off == 32  # 7 int32 = 28 bytes, pointer aligned to 8
+
+
+def test_geometry(kvq):
+    assert kvq.kvq_chunk_pad(1) == 64 and kvq.kvq_chunk_pad(64) == 64 and kvq.kvq_chunk_pad(4680) == 4736
+    assert kvq.kvq_chunk_pad(0) == 0
+    f = kvq.KvqFormat.make(2, "token", 128, True, "key")
+    assert kvq.window_shapes(f, 1, 40, 128, 4680, 8) == ((1, 40, 37888, 8), (1, 40, 37888))
+    f = kvq.KvqFormat.make(2, "token", 128, True, "value")
+    assert kvq.window_shapes(f, 1, 40, 128, 4680, 8) == ((1, 40, 592, 128, 4), (1, 40, 37888))
+    f = kvq.KvqFormat.make(4, "channel", 128, True, "key")
+    assert kvq.window_shapes(f, 1, 40, 128, 4680, 8) == ((1, 40, 37888, 16), (1, 40, 296, 128))
+    # bytes per token and head at d=128: INT2 32 + 4, INT4 64 + 4 (codes + fp16 step and zero)
+    assert 128 * 2 // 8 + 4 == 36 and 128 * 4 // 8 + 4 == 68
+
+
+def test_status_strings(kvq):
+    for st in range(0, -7, -1):
+        assert kvq.kvq_status_str(st) != "unknown status"
+    assert kvq.kvq_status_str(-99) == "unknown status"
+
+
+def test_pack_validation_without_launch(kvq):
+    lib = kvq._lib
+    p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    f = kvq.KvqFormat.make(2, "token", 128, True, "key")
+    call = lambda fmt, *a: lib.kvq_pack(*a[:5], ctypes.byref(fmt) if fmt else None, *a[5:])
+    assert call(f, None, 1, 1, 64, 128, 1, 0, p, p, p, None) == -1           # null input
+    assert call(None, p, 1, 1, 64, 128, 1, 0, p, p, p, None) == -1           # null format
+    assert call(f, p, 1, 1, 64, 96, 1, 0, p, p, p, None) == -2               # d
+    assert call(f, p, 0, 1, 64, 128, 1, 0, p, p, p, None) == -2              # B
+    assert call(f, p, 1, 1, 64, 128, 2, 2, p, p, p, None) == -2              # chunk_idx
+    assert call(kvq.KvqFormat.make(3, "token", 128, True, "key"), p, 1, 1, 64, 128, 1, 0, p, p, p, None) == -3
+    assert call(kvq.KvqFormat.make(2, "channel", 96, True, "key"), p, 1, 1, 64, 128, 1, 0, p, p, p, None) == -3
+    assert call(kvq.KvqFormat.make(2, "channel", 128, True, "value"), p, 1, 1, 64, 128, 1, 0, p, p, p, None) == -3
+    q = ctypes.c_void_p(18)
+    assert call(f, q, 1, 1, 64, 128, 1, 0, p, p, p, None) == -4              # misaligned
+
+
+def test_attn_validation_without_launch(kvq):
+    lib = kvq._lib
+    kf = kvq.KvqFormat.make(2, "token", 128, True, "key")
+    vf = kvq.KvqFormat.make(2, "token", 128, True, "value")
+    P = 4096
+
+    def args(**kw):
+        a = kvq.JbAttnArgs(1, 1, 128, 64, 64, 64, 1, P, P, P, P, P, P, P, P, P, kf, vf, 0.0, 1, P, None, None,
+                           None, 0)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    fwd = lambda a: lib.jb_attn_fwd(ctypes.byref(a), None)
+    mass = lambda a: lib.jb_attn_mass(ctypes.byref(a), None)
+    assert lib.jb_attn_fwd(None, None) == -1
+    assert fwd(args(d=96)) == -2
+    assert fwd(args(n_q=0)) == -2
+    assert fwd(args(n_chunks=0, n_r=0)) == -2
+    assert fwd(args(correction=7)) == -3
+    assert fwd(args(v_fmt=kvq.KvqFormat.make(4, "token", 128, True, "value"))) == -3
+    assert fwd(args(v_fmt=kf)) == -3
+    assert fwd(args(o=None)) == -1
+    assert fwd(args(k_codes=None)) == -1
+    assert fwd(args(mass_s=P)) == -1            # masses come in pairs
+    assert fwd(args(q=P + 2)) == -4
+    assert fwd(args(softmax_scale=-1.0)) == -2
+    assert mass(args()) == -1                   # mass needs mass_s / mass_r
+    assert lib.jb_attn_workspace_bytes(ctypes.byref(args())) == 0

@@ -1,0 +1,198 @@
+"""jb_attn_fwd / jb_attn_mass on the GPU vs the float64 oracle.
+
+The GPU packs the window itself (bit-exact with the oracle's quantizer, see
+test_gpu_pack.py), so both sides attend over identical dequantized inputs. Output
+tolerance: max|err|/rms <= 1e-2 and mean|err|/rms <= 1e-3 of the oracle's output;
+masses within 1e-3 and P_S + P_R = 1 within 1e-6.
+
+Small shapes are checked on every row; the full workloads run the full call on the
+GPU and check sampled rows of sampled heads (the oracle computes those rows exactly).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_kv_cache_kvq_amd import synth
+from tests.gpu_util import assert_attention_close, assert_mass_close, dev, lib_formats, oracle_formats
+
+pytestmark = pytest.mark.gpu
+
+
+def _kvq():
+    from bit_kv_cache_kvq_amd import kvq
+    return kvq
+
+
+def run_gpu(x, w, *, k_had=True, v_had=True, bits=None, correction=1, masses=True, mass_only=False, scale=0.0):
+    """Pack the window and run one call; returns numpy (O, P_S, P_R)."""
+    kvq = _kvq()
+    kf, vf = lib_formats(w, k_had, v_had, bits)
+    q, kr, vr = dev(x["q"]), dev(x["k_cur"]), dev(x["v_cur"])
+    if w.n_chunks > 0:
+        kwin = kvq.pack_window(dev(x["k_cache"]), w.chunk_len, kf)
+        vwin = kvq.pack_window(dev(x["v_cache"]), w.chunk_len, vf)
+    else:
+        kwin = vwin = None
+    B, H, n_q, d = x["q"].shape
+    o = torch.empty((B, H, n_q, d), dtype=torch.float32, device="cuda")
+    ms = torch.empty((B, H, n_q), dtype=torch.float32, device="cuda") if masses or mass_only else None
+    mr = torch.empty((B, H, n_q), dtype=torch.float32, device="cuda") if masses or mass_only else None
+    args = kvq.make_args(q, kr if x["k_cur"].shape[2] else None, vr if x["k_cur"].shape[2] else None, kwin, vwin,
+                         w.chunk_len, w.n_chunks, kf, vf, o=o, mass_s=ms, mass_r=mr, correction=correction,
+                         softmax_scale=scale)
+    if mass_only:
+        kvq.jb_attn_mass(args)
+    else:
+        kvq.jb_attn_fwd(args)
+    torch.cuda.synchronize()
+    return (o.cpu().numpy(), ms.cpu().numpy() if ms is not None else None, mr.cpu().numpy() if mr is not None else None)
+
+
+def run_oracle(x, w, rows=None, heads=None, *, k_had=True, v_had=True, bits=None, correction="taylor", scale=None):
+    kf, vf = oracle_formats(w, k_had, v_had, bits)
+    if heads is not None:
+        x = {k: np.stack([v[b, h] for (b, h) in heads])[None] for k, v in x.items()}
+    O, PS, PR, _ = oracle.reference_call(x["q"], x["k_cache"], x["v_cache"], x["k_cur"], x["v_cur"],
+                                         chunk_len=w.chunk_len, k_fmt=kf, v_fmt=vf, correction=correction,
+                                         rows=rows, softmax_scale=scale)
+    return O, PS, PR
+
+
+def _gather(a, heads, rows):
+    return np.stack([a[b, h][rows] for (b, h) in heads])[None]
+
+
+@pytest.mark.parametrize("correction", [1, 0])
+def test_tiny_all_rows(correction):
+    w = synth.WORKLOADS["tiny"]
+    print(f"attn tiny correction={correction}", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w, correction=correction)
+    Or, PSr, PRr = run_oracle(x, w, correction="taylor" if correction else "none")
+    assert_attention_close(O, Or, f"tiny c={correction}")
+    assert_mass_close(PS, PR, PSr, PRr, f"tiny c={correction}")
+
+
+# (name, rows per sampled head)
+FULL = [("c24", 96), ("c40", 64), ("long", 32)]
+
+
+@pytest.mark.parametrize("name,nrows", FULL)
+def test_workload_sampled_rows(name, nrows):
+    w = synth.WORKLOADS[name]
+    print(f"attn {name}: full call, oracle on {nrows} rows x 2 heads", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w, masses=True)
+    rng = np.random.default_rng(5)
+    rows = np.sort(np.concatenate([[0, w.n_q - 1], rng.choice(w.n_q, nrows - 2, replace=False)]))
+    heads = [(0, 1), (w.B - 1, w.H - 2)]
+    Or, PSr, PRr = run_oracle(x, w, rows=rows, heads=heads)
+    assert_attention_close(_gather(O, heads, rows), Or, name)
+    assert_mass_close(_gather(PS, heads, rows), _gather(PR, heads, rows), PSr, PRr, name)
+    assert np.all(np.isfinite(O))
+
+
+def test_c40_int4_sampled_rows():
+    w = synth.WORKLOADS["c40"].replace(bits=4)
+    print("attn c40 int4", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w)
+    rows = np.arange(0, w.n_q, 97)
+    heads = [(0, 5)]
+    Or, PSr, PRr = run_oracle(x, w, rows=rows, heads=heads)
+    assert_attention_close(_gather(O, heads, rows), Or, "c40 int4")
+    assert_mass_close(_gather(PS, heads, rows), _gather(PR, heads, rows), PSr, PRr, "c40 int4")
+
+
+# ragged and degenerate shapes, every row checked
+EDGES = [
+    dict(B=1, H=2, d=64, n_q=300, chunk_len=100, n_chunks=3),      # ragged queries, chunks, tiles
+    dict(B=2, H=1, d=128, n_q=257, chunk_len=64, n_chunks=2),      # one query past a block
+    dict(B=1, H=1, d=128, n_q=1, chunk_len=1, n_chunks=5),         # single query, one-token chunks
+    dict(B=1, H=3, d=128, n_q=70, chunk_len=130, n_chunks=0),      # no cache: current chunk only
+    dict(B=1, H=1, d=64, n_q=40, chunk_len=33, n_chunks=4),
+]
+
+
+@pytest.mark.parametrize("shape", EDGES, ids=lambda s: "x".join(str(v) for v in s.values()))
+@pytest.mark.parametrize("bits", [2, 4])
+def test_edges_all_rows(shape, bits):
+    w = synth.Workload("edge", **shape, bits=bits, seed=3)
+    print(f"attn edge {shape} bits={bits}", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w)
+    Or, PSr, PRr = run_oracle(x, w)
+    assert_attention_close(O, Or, f"edge {shape}")
+    assert_mass_close(PS, PR, PSr, PRr, f"edge {shape}")
+
+
+def test_no_current_chunk():
+    w = synth.Workload("nocur", B=1, H=2, d=128, n_q=100, chunk_len=96, n_chunks=2)
+    x = synth.draw_all(w)
+    x["k_cur"] = x["k_cur"][:, :, :0]
+    x["v_cur"] = x["v_cur"][:, :, :0]
+    print("attn no current chunk", flush=True)
+    O, PS, PR = run_gpu(x, w)
+    Or, PSr, PRr = run_oracle(x, w)
+    assert_attention_close(O, Or, "no current")
+    np.testing.assert_allclose(PS, 1.0, atol=1e-6)
+
+
+@pytest.mark.parametrize("k_had,v_had", [(0, 0), (1, 0), (0, 1)])
+def test_rotation_flags(k_had, v_had):
+    w = synth.Workload("rot", B=1, H=2, d=128, n_q=200, chunk_len=150, n_chunks=2)
+    x = synth.draw_all(w)
+    print(f"attn rotation k={k_had} v={v_had}", flush=True)
+    O, PS, PR = run_gpu(x, w, k_had=k_had, v_had=v_had)
+    Or, PSr, PRr = run_oracle(x, w, k_had=bool(k_had), v_had=bool(v_had))
+    assert_attention_close(O, Or, f"rot {k_had}{v_had}")
+    assert_mass_close(PS, PR, PSr, PRr, f"rot {k_had}{v_had}")
+
+
+def test_softmax_scale_argument():
+    w = synth.Workload("scale", B=1, H=1, d=64, n_q=64, chunk_len=64, n_chunks=2)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w, scale=0.05)
+    Or, PSr, PRr = run_oracle(x, w, scale=0.05)
+    assert_attention_close(O, Or, "scale")
+
+
+def test_mass_only_matches_forward():
+    w = synth.WORKLOADS["c24"]
+    x = synth.draw_all(w, heads=None)
+    print("attn mass-only c24", flush=True)
+    O, PS, PR = run_gpu(x, w)
+    _, PS2, PR2 = run_gpu(x, w, mass_only=True)
+    np.testing.assert_allclose(PS2, PS, atol=2e-6)
+    np.testing.assert_allclose(PR2, PR, atol=2e-6)
+
+
+def test_deterministic():
+    w = synth.WORKLOADS["c24"]
+    x = synth.draw_all(w)
+    print("attn determinism c24", flush=True)
+    a = run_gpu(x, w)
+    b = run_gpu(x, w)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_rejects_bad_arguments():
+    kvq = _kvq()
+    w = synth.WORKLOADS["tiny"]
+    kf, vf = lib_formats(w)
+    q = torch.zeros((1, 2, 128, 64), dtype=torch.int16, device="cuda")
+    o = torch.empty((1, 2, 128, 64), dtype=torch.float32, device="cuda")
+    kwin = kvq.alloc_window(kf, 1, 2, 64, 128, 2)
+    vwin = kvq.alloc_window(vf, 1, 2, 64, 128, 2)
+    bad_v = kvq.KvqFormat.make(4, "token", 128, True, "value")       # mixed bits
+    args = kvq.make_args(q, q, q, kwin, vwin, 128, 2, kf, bad_v, o=o)
+    with pytest.raises(kvq.KvqError):
+        kvq.jb_attn_fwd(args)
+    args = kvq.make_args(q, q, q, kwin, vwin, 128, 2, vf, vf, o=o)    # key window with value role
+    with pytest.raises(kvq.KvqError):
+        kvq.jb_attn_fwd(args)
+    args = kvq.make_args(q, q, q, kwin, vwin, 128, 2, kf, vf, o=None)  # fwd needs o
+    with pytest.raises(kvq.KvqError):
+        kvq.jb_attn_fwd(args)

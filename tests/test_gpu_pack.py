@@ -60,9 +60,9 @@ def _edge_input(n_tok, d, seed):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((2, 3, n_tok, d)).astype(np.float32)
     x[..., :3] *= 10
-    x[0, 0, 5, :] = 0.75                        # constant token: Delta = 0
-    x[0, 1, 7, :] = np.linspace(-3, -2, d)      # range entirely negative: z outside [0, 3]
-    x[1, 2, 9, :] = np.linspace(2, 2.001, d)    # tiny positive range
+    x[0, 0, 5 % n_tok, :] = 0.75                        # constant token: Delta = 0
+    x[0, 1, 7 % n_tok, :] = np.linspace(-3, -2, d)      # range entirely negative: z outside [0, 3]
+    x[1, 2, 9 % n_tok, :] = np.linspace(2, 2.001, d)    # tiny positive range
     x[1, 0, :, 7] = 1e-3                        # a near-constant channel (per-channel groups)
     return synth.f32_to_bf16_bits(x)
 

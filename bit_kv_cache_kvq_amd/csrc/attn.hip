@@ -10,16 +10,23 @@
 // s^2 |q|^2 Delta_j^2 / 24).
 //
 // Kernel design (one workgroup = 8 waves = 256 queries of one head; a wave owns 32
-// queries and streams 64-key tiles):
+// queries and streams 64-key tiles through a two-stage LDS pipeline, one barrier per
+// tile, the next tile's global loads in flight during the current tile's math):
 //  * Scores are computed transposed, S^T = K Q^T, so keys are the MFMA M dimension and
 //    each lane owns one query: per-query softmax state lives in one lane (and its
 //    partner lane l^32, which holds the other half of each key block).
 //  * Cached QK^T runs on int8 MFMA (v_mfma_i32_32x32x32_i8): the rotated query
-//    q' = H q is a 16-bit fixed-point integer split into signed hi/lo bytes, the key
-//    operand is the raw 2- or 4-bit code, unpacked in registers with shifts and masks.
-//    Integer accumulation is exact; the zero point enters as -z_j * sum(q_fixed).
-//    Logit (log2 units): x = Delta_j (A S - G Delta_j), A = s sigma log2(e),
-//    G = s^2 |q'|^2 / 24 log2(e).
+//    q' = H q is a 16-bit fixed-point integer (scale sigma) split into signed hi/lo
+//    bytes, the key operand is the raw 2- or 4-bit code, unpacked in registers with
+//    shifts and masks; integer accumulation is exact: S = 256 S_hi + S_lo.
+//  * The zero point and the correction enter through one fp16 MFMA per 32x32 block whose
+//    key operand is (z_j, z_j, Delta_j, Delta_j) and whose query operand is the hi/lo
+//    fp16 split of (-A sum(q_fixed), -G): bias_ij = -A z_j sum(q_fixed) - G Delta_j.
+//    Logit in log2 units: x = Delta_j (A S + bias), A = s sigma log2 e,
+//    G = s^2 |q'|^2 / 24 log2 e.
+//  * Softmax with a lazy running max m: p = exp2(Delta_j * inner - m) in one fma and one
+//    exp; the exact max and the rescale run only when a tile's p exceeds 2^8 (or for a
+//    ragged tile), so P values stay below 2^8 and in fp16 range.
 //  * PV runs on fp16 MFMA: P~ = p Delta^V_j rounded to fp16, times (code - z) exact in
 //    fp16, unpacked once per workgroup into LDS (channel-major rows). A fixed key
 //    permutation inside each 32-key block lets P~ feed the B operand straight from the
@@ -39,6 +46,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 8;
@@ -47,6 +55,7 @@ constexpr int kBM = 32 * kWaves;  // queries per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kQFix = 32639.f;  // |q_fixed| <= 32639 keeps hi = (q+128)>>8 in int8
+constexpr float kLazy = 256.f;    // 2^8: largest p allowed before the running max is raised
 
 struct Params {
   int B, H, n_q, n_r, chunk_len, n_chunks, cp;
@@ -86,14 +95,17 @@ __device__ __host__ constexpr int kperm(int j, int b) {
   return BITS == 2 ? 4 * b + j : 8 * (j >> 1) + 2 * b + (j & 1);
 }
 
-__device__ inline float half_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ inline float half_bits_to_f32(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
 __device__ inline uint32_t pack_f16x2(float lo, float hi) {
-  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  f16x2 r;
+  r[0] = (_Float16)lo;
+  r[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32); }
+__device__ inline float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Map a linear workgroup id to (query block, head) so that all query blocks of a head
 // run on the same XCD (workgroups are dealt to the 8 XCDs round-robin), keeping that
@@ -109,27 +121,34 @@ __device__ inline void xcd_map(int L, int total, int n_qblk, int& qb, int& bh) {
 }
 
 template <int D, int BITS>
+struct TileBuf {
+  static constexpr int KW = D * BITS / 32;  // key words per token
+  static constexpr int VROW = kBN + 8;      // fp16 per value row (padded against bank conflicts)
+  alignas(16) uint32_t k_words[kBN][KW];    // cached keys, natural token order
+  alignas(16) _Float16 v[D][VROW];          // (code - z) or current-chunk values, channel-major
+  alignas(16) uint16_t kr[kBN][D + 8];      // current-chunk keys (bf16), natural order
+  alignas(16) float dk[kBN];                // per key, M-row order
+  alignas(16) float dv[kBN];
+  alignas(16) float mask[kBN];
+  alignas(16) uint2 kb[kBN];                // bias operand: (z, z), (Delta, Delta) as fp16
+};
+
+template <int D, int BITS>
 struct Smem {
-  static constexpr int KW = D * BITS / 32;           // key words per token
-  static constexpr int VROW = kBN + 8;               // fp16 per V row (padded)
-  uint32_t k_words[kBN][KW];
-  _Float16 v[D][VROW];                               // (code - z) or current-chunk values
-  uint16_t kr[kBN][D + 8];                           // current-chunk keys (bf16)
-  float dk[kBN];                                     // per key, M-row order
-  int zk[kBN];
-  float dv[kBN];
-  float mask[kBN];
-  uint32_t zv_pair[kBN / 2];                         // (-1024 - z) fp16 pairs, natural order
+  TileBuf<D, BITS> buf[2];
+  alignas(16) uint32_t zv_pair[2][kBN / 2];  // (-1024 - z) fp16 pairs of a tile's value tokens
 };
 
 template <int D, int BITS, bool MASS_ONLY>
 __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   constexpr int HALF = D / 2;
-  constexpr int KSTEPS = D / 32;        // int8 K-steps of 32 channels
-  constexpr int CBLK = D / 32;          // 32-channel output blocks
+  constexpr int KSTEPS = D / 32;  // int8 K-steps of 32 channels
+  constexpr int CBLK = D / 32;    // 32-channel output blocks
   constexpr int CPW = 32 / BITS;
-  constexpr int KW = D * BITS / 32;     // key words per token
-  constexpr int VWPC = kBN / CPW;       // value words per channel per 64-token block
+  constexpr int KW = D * BITS / 32;    // key words per token
+  constexpr int VWPC = kBN / CPW;      // value words per channel per 64-token block
+  constexpr int KWT = kBN * KW;        // key words per tile
+  constexpr int VWT = D * VWPC;        // value words per tile
   __shared__ Smem<D, BITS> sm;
 
   const int tid = threadIdx.x;
@@ -142,14 +161,15 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
 
   // ---------------- prologue: rotated query as 16-bit fixed point, hi/lo bytes --------
   i32x4 qhi[KSTEPS], qlo[KSTEPS];
-  float A, G;
-  int nqsum;
+  f16x8 qbias;  // B operand of the bias MFMA
+  float A;
   {
     float qv[HALF];
     const uint16_t* qrow = p.q + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h;
 #pragma unroll
     for (int u = 0; u < HALF / 8; u++) {
-      uint4 w = q_ok ? reinterpret_cast<const uint4*>(qrow)[u] : make_uint4(0, 0, 0, 0);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (q_ok) w = reinterpret_cast<const uint4*>(qrow)[u];
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; e++) {
@@ -203,9 +223,20 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         qlo[kk][j] = (int)wlo;
       }
     qs += __shfl_xor(qs, 32);
-    nqsum = -qs;
     A = p.s * sigma * kLog2e;
-    G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
+    const float G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
+    // bias = z_j * (-A qs) + Delta_j * (-G), each factor split into fp16 hi + lo
+    const float bz = -A * (float)qs, bd = -G;
+    const _Float16 bz_hi = (_Float16)bz, bd_hi = (_Float16)bd;
+    const _Float16 bz_lo = (_Float16)(bz - (float)bz_hi), bd_lo = (_Float16)(bd - (float)bd_hi);
+#pragma unroll
+    for (int e = 0; e < 8; e++) qbias[e] = (_Float16)0.f;
+    if (h == 0) {
+      qbias[0] = bz_hi;
+      qbias[1] = bz_lo;
+      qbias[2] = bd_hi;
+      qbias[3] = bd_lo;
+    }
   }
 
   float m_run = -INFINITY, l_s = 0.f, l_r = 0.f;
@@ -215,9 +246,9 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
 #pragma unroll
     for (int v = 0; v < 16; v++) acc[c][v] = 0.f;
 
-  // Online-softmax step over one 64-key tile whose scores (log2 units) are in x[2][16].
-  // Returns p in x; updates m_run and rescales acc and the sums when the max grows.
-  auto softmax_tile = [&](float (&x)[2][16]) {
+  // Exact max + rescale for a tile whose logits x (log2 units, masked) are given; the
+  // returned x hold p = exp2(x - m_run).
+  auto exact_tile = [&](float (&x)[2][16]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; mb++)
@@ -226,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     mx = fmaxf(mx, xor32(mx));
     const float m_new = fmaxf(m_run, mx);
     if (__ballot(m_new > m_run) != 0) {
-      const float sc = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float sc = exp2_(m_run - m_new);
       l_s *= sc;
       l_r *= sc;
       if (!MASS_ONLY) {
@@ -240,111 +271,190 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
 #pragma unroll
     for (int mb = 0; mb < 2; mb++)
 #pragma unroll
-      for (int v = 0; v < 16; v++) x[mb][v] = __builtin_amdgcn_exp2f(x[mb][v] - m_run);
+      for (int v = 0; v < 16; v++) x[mb][v] = exp2_(x[mb][v] - m_run);
   };
 
-  // PV for one tile: B operand = P (fp16 pairs from the score registers), A = V rows in LDS.
-  auto pv_tile = [&](const uint32_t (&pb)[4][4]) {
+  // PV for one tile: B operand = P (fp16 pairs from the score registers), A = value rows in LDS.
+  auto pv_tile = [&](const TileBuf<D, BITS>& tb, const uint32_t (&pb)[4][4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
       const f16x8 bop = __builtin_bit_cast(f16x8, make_uint4(pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]));
 #pragma unroll
       for (int c = 0; c < CBLK; c++) {
-        const f16x8 aop = *reinterpret_cast<const f16x8*>(&sm.v[32 * c + col][16 * ks + 8 * h]);
+        const f16x8 aop = *reinterpret_cast<const f16x8*>(&tb.v[32 * c + col][16 * ks + 8 * h]);
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, acc[c], 0, 0, 0);
       }
     }
   };
 
   // ---------------- phase 1: cached window ----------------
-  const int n_tiles = p.n_chunks * (p.cp / kBN);
+  const int tiles_per_chunk = p.cp / kBN;
+  const int n_tiles = p.n_chunks * tiles_per_chunk;
   const size_t n_tot = (size_t)p.n_chunks * p.cp;
   const uint32_t* kc_base = p.k_codes + (size_t)bh * n_tot * KW;
-  const uint32_t* vc_base = p.v_codes + (size_t)bh * (n_tot / kBN) * (D * VWPC);
+  const uint32_t* vc_base = p.v_codes + (size_t)bh * (n_tot / kBN) * VWT;
   const uint16_t* ks_base = p.k_scale + (size_t)bh * n_tot;
   const uint16_t* kz_base = p.k_zero + (size_t)bh * n_tot;
   const uint16_t* vs_base = p.v_scale + (size_t)bh * n_tot;
   const uint16_t* vz_base = p.v_zero + (size_t)bh * n_tot;
 
-  for (int T = 0; T < n_tiles; T++) {
-    const int off = (T * kBN) % p.cp;
-    const int nvalid = min(kBN, p.chunk_len - off);
-    const size_t tok0 = (size_t)T * kBN;
-    __syncthreads();  // the previous tile's LDS reads are complete
-    // stage packed key words (natural token order)
-    for (int e = tid; e < kBN * KW; e += kThreads) (&sm.k_words[0][0])[e] = kc_base[tok0 * KW + e];
-    if (tid < kBN) {
-      const int j = tid;
-      const int r = 32 * (j >> 5) + key_mrow(j & 31);
-      const float dk = half_bits_to_f32(ks_base[tok0 + j]);
-      const float zk = half_bits_to_f32(kz_base[tok0 + j]);
-      const float dv = MASS_ONLY ? 0.f : half_bits_to_f32(vs_base[tok0 + j]);
-      sm.dk[r] = dk;
-      sm.zk[r] = (int)zk;
-      sm.dv[r] = dv;
-      sm.mask[r] = j < nvalid ? 0.f : -INFINITY;
-    }
-    if (!MASS_ONLY && tid < kBN / 2) {
-      // pair (j, j+8) of each 16-token group: halves hold -(1024 + z)
-      const int g = tid >> 3, j = tid & 7;
-      const float z0 = half_bits_to_f32(vz_base[tok0 + 16 * g + j]);
-      const float z1 = half_bits_to_f32(vz_base[tok0 + 16 * g + j + 8]);
-      sm.zv_pair[tid] = pack_f16x2(-1024.f - z0, -1024.f - z1);
-    }
-    __syncthreads();
-    if (!MASS_ONLY) {
-      // unpack value codes into (code - z) fp16, channel-major rows, pair-interleaved
-      const uint32_t* vblk = vc_base + (size_t)T * (D * VWPC);
-      for (int e = tid; e < D * (kBN / 16); e += kThreads) {
-        const int ch = e / (kBN / 16), g = e % (kBN / 16);  // 16-token group g of channel ch
-        uint32_t out[8];
-        if (BITS == 2) {
-          const uint32_t w = vblk[ch * VWPC + g];
-#pragma unroll
-          for (int j = 0; j < 8; j++) out[j] = ((w >> (2 * j)) & 0x00030003u) | 0x64006400u;
-        } else {
-          const uint32_t w0 = vblk[ch * VWPC + 2 * g], w1 = vblk[ch * VWPC + 2 * g + 1];
-          // t0 = [w0.b0 w0.b1 w1.b0 w1.b1], t1 = [w0.b2 w0.b3 w1.b2 w1.b3]
-          const uint32_t t0 = (w0 & 0xFFFFu) | (w1 << 16);
-          const uint32_t t1 = (w0 >> 16) | (w1 & 0xFFFF0000u);
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            out[j] = ((t0 >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-            out[4 + j] = ((t1 >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-          }
-        }
-        uint32_t res[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-          const h2 a = __builtin_bit_cast(h2, out[j]);
-          const h2 z = __builtin_bit_cast(h2, sm.zv_pair[8 * g + j]);
-          res[j] = __builtin_bit_cast(uint32_t, a + z);
-        }
-        uint4* dst = reinterpret_cast<uint4*>(&sm.v[ch][16 * g]);
-        dst[0] = make_uint4(res[0], res[1], res[2], res[3]);
-        dst[1] = make_uint4(res[4], res[5], res[6], res[7]);
-      }
-      __syncthreads();
-    }
 
-    // ---- QK^T on int8 MFMA ----
+  // ---- prefetch registers: key words, one 16-token group of value words, per-key fp16 ----
+  constexpr int KPT = KWT >= kThreads ? KWT / kThreads : 1;  // key words per thread (contiguous)
+  constexpr int WPG = BITS / 2;                                // value words per 16-token group
+  constexpr int VGT = D * (kBN / 16);                          // value groups per tile (<= kThreads)
+  static_assert(KWT <= 2 * kThreads && VGT <= kThreads, "tile staging assumes at most 2 words per thread");
+  uint32_t kwr[KPT], vwr[WPG];
+  uint32_t pk_dk = 0, pk_zk = 0, pk_dv = 0;  // per-key fp16 bits (threads < kBN)
+  uint32_t pz0 = 0, pz1 = 0;                 // value zero points of a token pair (threads < kBN/2)
+#pragma unroll
+  for (int e = 0; e < KPT; e++) kwr[e] = 0;
+#pragma unroll
+  for (int e = 0; e < WPG; e++) vwr[e] = 0;
+
+  auto load_tile = [&](int T) {
+    const size_t tok0 = (size_t)T * kBN;
+    if (tid * KPT < KWT) {
+      const uint32_t* src = kc_base + tok0 * KW + tid * KPT;
+      if constexpr (KPT == 2) {
+        const uint2 w = *reinterpret_cast<const uint2*>(src);
+        kwr[0] = w.x;
+        kwr[KPT - 1] = w.y;
+      } else {
+        kwr[0] = src[0];
+      }
+    }
+    if (!MASS_ONLY && tid < VGT) {
+      const uint32_t* src = vc_base + (size_t)T * VWT + tid * WPG;
+      if constexpr (WPG == 2) {
+        const uint2 w = *reinterpret_cast<const uint2*>(src);
+        vwr[0] = w.x;
+        vwr[WPG - 1] = w.y;
+      } else {
+        vwr[0] = src[0];
+      }
+    }
+    if (tid < kBN) {
+      pk_dk = ks_base[tok0 + tid];
+      pk_zk = kz_base[tok0 + tid];
+      if (!MASS_ONLY) pk_dv = vs_base[tok0 + tid];
+    }
+  };
+  auto load_zv = [&](int T) {
+    if (!MASS_ONLY && tid < kBN / 2) {
+      const size_t tok0 = (size_t)T * kBN;
+      const int g = tid >> 3, j = tid & 7;
+      pz0 = vz_base[tok0 + 16 * g + j];
+      pz1 = vz_base[tok0 + 16 * g + j + 8];
+    }
+  };
+  auto store_zv = [&](int slot) {
+    if (!MASS_ONLY && tid < kBN / 2)
+      sm.zv_pair[slot][tid] = pack_f16x2(-1024.f - half_bits_to_f32(pz0), -1024.f - half_bits_to_f32(pz1));
+  };
+  // Key words, per-key values and the unpacked value tile of tile T (its zero-point
+  // pairs must already be visible in zv_pair[T & 1]).
+  auto store_tile = [&](int T, TileBuf<D, BITS>& tb) {
+    if (tid * KPT < KWT) {
+      uint32_t* dst = &tb.k_words[0][0] + tid * KPT;
+      if constexpr (KPT == 2)
+        *reinterpret_cast<uint2*>(dst) = make_uint2(kwr[0], kwr[KPT - 1]);
+      else
+        dst[0] = kwr[0];
+    }
+    if (tid < kBN) {
+      const int r = 32 * (tid >> 5) + key_mrow(tid & 31);
+      const int nvalid = min(kBN, p.chunk_len - (T % tiles_per_chunk) * kBN);
+      tb.dk[r] = half_bits_to_f32(pk_dk);
+      tb.dv[r] = half_bits_to_f32(pk_dv);
+      tb.mask[r] = tid < nvalid ? 0.f : -INFINITY;
+      tb.kb[r] = make_uint2((pk_zk & 0xFFFFu) | (pk_zk << 16), (pk_dk & 0xFFFFu) | (pk_dk << 16));
+    }
+    if (!MASS_ONLY && tid < VGT) {
+      const int ch = tid >> 2, g = tid & 3;  // 16-token group g of channel ch
+      const uint4* zp = reinterpret_cast<const uint4*>(&sm.zv_pair[T & 1][8 * g]);
+      const uint4 z0 = zp[0], z1 = zp[1];
+      const uint32_t zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      uint32_t a[8];
+      if constexpr (BITS == 2) {
+        const uint32_t w = vwr[0];
+#pragma unroll
+        for (int j = 0; j < 8; j++) a[j] = ((w >> (2 * j)) & 0x00030003u) | 0x64006400u;
+      } else {
+        // t0 = [w0.b0 w0.b1 w1.b0 w1.b1], t1 = [w0.b2 w0.b3 w1.b2 w1.b3]
+        const uint32_t w0 = vwr[0], w1 = vwr[WPG - 1];
+        const uint32_t t0 = (w0 & 0xFFFFu) | (w1 << 16);
+        const uint32_t t1 = (w0 >> 16) | (w1 & 0xFFFF0000u);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          a[j] = ((t0 >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+          a[4 + j] = ((t1 >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+        }
+      }
+      uint32_t res[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        res[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a[j]) + __builtin_bit_cast(f16x2, zz[j]));
+      uint4* dst = reinterpret_cast<uint4*>(&tb.v[ch][16 * g]);
+      dst[0] = make_uint4(res[0], res[1], res[2], res[3]);
+      dst[1] = make_uint4(res[4], res[5], res[6], res[7]);
+    }
+  };
+
+  // Lazy softmax over one tile: inner scores are turned into p = exp2(scale*inner - m)
+  // by one fma and one exp when that keeps every p <= 2^8; otherwise (and for ragged
+  // tiles, which need the mask) the exact max path runs. scl[mb][v] multiplies inner.
+  auto softmax_tile = [&](const f32x16 (&inner)[2], const float (&scl)[2][16], bool ragged,
+                          const float* mask_rows, float (&pv)[2][16]) {
+    bool fast = !ragged;
+    if (fast) {
+      float pmax = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          pv[mb][v] = exp2_(fmaf(scl[mb][v], inner[mb][v], -m_run));
+          pmax = fmaxf(pmax, pv[mb][v]);
+        }
+      pmax = fmaxf(pmax, xor32(pmax));
+      fast = __ballot(!(pmax <= kLazy)) == 0;
+    }
+    if (!fast) {
+#pragma unroll
+      for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          pv[mb][v] = scl[mb][v] * inner[mb][v];
+          if (ragged) pv[mb][v] += mask_rows[32 * mb + (v & 3) + 8 * (v >> 2) + 4 * h];
+        }
+      exact_tile(pv);
+    }
+  };
+
+  auto compute_cached = [&](int T, const TileBuf<D, BITS>& tb) {
+    const int nvalid = min(kBN, p.chunk_len - (T % tiles_per_chunk) * kBN);
     i32x16 shi[2], slo[2];
+    f32x16 inner[2];
 #pragma unroll
     for (int mb = 0; mb < 2; mb++) {
       const int key = 32 * mb + mrow_key(col);
       uint32_t kw[KW / 2];
-#pragma unroll
-      for (int e = 0; e < KW / 2; e++) kw[e] = sm.k_words[key][(KW / 2) * h + e];
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        shi[mb][v] = 0;
-        slo[mb][v] = 0;
+      if constexpr (KW / 2 == 4) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&tb.k_words[key][(KW / 2) * h]);
+        kw[0] = w.x; kw[1] = w.y; kw[2] = w.z; kw[3] = w.w;
+      } else if constexpr (KW / 2 == 8) {
+        const uint4 w0 = *reinterpret_cast<const uint4*>(&tb.k_words[key][(KW / 2) * h]);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(&tb.k_words[key][(KW / 2) * h + 4]);
+        kw[0] = w0.x; kw[1] = w0.y; kw[2] = w0.z; kw[3] = w0.w;
+        kw[4 % (KW / 2)] = w1.x; kw[5 % (KW / 2)] = w1.y; kw[6 % (KW / 2)] = w1.z; kw[7 % (KW / 2)] = w1.w;
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(&tb.k_words[key][(KW / 2) * h]);
+        kw[0] = w.x; kw[1 % (KW / 2)] = w.y;
       }
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; kk++) {
         i32x4 aop;
-        if (BITS == 2) {
+        if constexpr (BITS == 2) {
           const uint32_t w = kw[kk];
 #pragma unroll
           for (int j = 0; j < 4; j++) aop[j] = (int)((w >> (2 * j)) & 0x03030303u);
@@ -355,53 +465,74 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
           aop[2] = (int)(w1 & 0x0F0F0F0Fu);
           aop[3] = (int)((w1 >> 4) & 0x0F0F0F0Fu);
         }
-        shi[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, qhi[kk], shi[mb], 0, 0, 0);
-        slo[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, qlo[kk], slo[mb], 0, 0, 0);
+        if (kk == 0) {
+          const i32x16 z = {};
+          shi[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, qhi[kk], z, 0, 0, 0);
+          slo[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, qlo[kk], z, 0, 0, 0);
+        } else {
+          shi[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, qhi[kk], shi[mb], 0, 0, 0);
+          slo[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, qlo[kk], slo[mb], 0, 0, 0);
+        }
       }
+      const uint2 kb = tb.kb[32 * mb + col];
+      const f16x8 bop = __builtin_bit_cast(f16x8, make_uint4(kb.x, kb.y, 0u, 0u));
+      const f32x16 zf = {};
+      inner[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bop, qbias, zf, 0, 0, 0);
     }
-    // ---- logits with the correction ----
-    float x[2][16];
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) inner[mb][v] = fmaf(A, (float)((shi[mb][v] << 8) + slo[mb][v]), inner[mb][v]);
+    float dk[2][16];
 #pragma unroll
     for (int mb = 0; mb < 2; mb++)
 #pragma unroll
       for (int v4 = 0; v4 < 4; v4++) {
-        const int r0 = 32 * mb + 8 * v4 + 4 * h;
-        const float4 dk4 = *reinterpret_cast<const float4*>(&sm.dk[r0]);
-        const int4 zk4 = *reinterpret_cast<const int4*>(&sm.zk[r0]);
-        const float dk[4] = {dk4.x, dk4.y, dk4.z, dk4.w};
-        const int zk[4] = {zk4.x, zk4.y, zk4.z, zk4.w};
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-          const int v = 4 * v4 + b;
-          const int si = (shi[mb][v] << 8) + slo[mb][v] + zk[b] * nqsum;
-          const float f = (float)si;
-          x[mb][v] = dk[b] * fmaf(A, f, -G * dk[b]);
-        }
+        const float4 d4 = *reinterpret_cast<const float4*>(&tb.dk[32 * mb + 8 * v4 + 4 * h]);
+        dk[mb][4 * v4] = d4.x; dk[mb][4 * v4 + 1] = d4.y; dk[mb][4 * v4 + 2] = d4.z; dk[mb][4 * v4 + 3] = d4.w;
       }
-    if (nvalid < kBN) {
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-        for (int v = 0; v < 16; v++) x[mb][v] += sm.mask[32 * mb + (v & 3) + 8 * (v >> 2) + 4 * h];
-    }
-    softmax_tile(x);
+    float pv[2][16];
+    softmax_tile(inner, dk, nvalid < kBN, tb.mask, pv);
 #pragma unroll
     for (int mb = 0; mb < 2; mb++)
 #pragma unroll
-      for (int v = 0; v < 16; v++) l_s += x[mb][v];
+      for (int v = 0; v < 16; v++) l_s += pv[mb][v];
     if (!MASS_ONLY) {
       uint32_t pb[4][4];
 #pragma unroll
       for (int mb = 0; mb < 2; mb++)
 #pragma unroll
         for (int v4 = 0; v4 < 4; v4++) {
-          const float4 dv4 = *reinterpret_cast<const float4*>(&sm.dv[32 * mb + 8 * v4 + 4 * h]);
+          const float4 dv4 = *reinterpret_cast<const float4*>(&tb.dv[32 * mb + 8 * v4 + 4 * h]);
           const int v = 4 * v4;
           const int ks = 2 * mb + (v4 >> 1), slot = 2 * (v4 & 1);
-          pb[ks][slot] = pack_f16x2(x[mb][v] * dv4.x, x[mb][v + 1] * dv4.y);
-          pb[ks][slot + 1] = pack_f16x2(x[mb][v + 2] * dv4.z, x[mb][v + 3] * dv4.w);
+          pb[ks][slot] = pack_f16x2(pv[mb][v] * dv4.x, pv[mb][v + 1] * dv4.y);
+          pb[ks][slot + 1] = pack_f16x2(pv[mb][v + 2] * dv4.z, pv[mb][v + 3] * dv4.w);
         }
-      pv_tile(pb);
+      pv_tile(tb, pb);
+    }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    load_zv(0);
+    store_zv(0);
+    if (n_tiles > 1) {
+      load_zv(1);
+      store_zv(1);
+    }
+    __syncthreads();
+    store_tile(0, sm.buf[0]);
+    __syncthreads();
+    for (int T = 0; T < n_tiles; T++) {
+      const int cur = T & 1;
+      const bool has_next = T + 1 < n_tiles;
+      if (has_next) load_tile(T + 1);
+      if (T + 2 < n_tiles) load_zv(T + 2);
+      compute_cached(T, sm.buf[cur]);
+      if (has_next) store_tile(T + 1, sm.buf[cur ^ 1]);
+      if (T + 2 < n_tiles) store_zv(cur);  // tile T+2 uses slot (T+2) & 1 == cur
+      __syncthreads();
     }
   }
 
@@ -409,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   if (!MASS_ONLY && p.v_had && n_tiles > 0) {
     // acc[c][v] holds channel 32c + (v&3) + 8(v>>2) + 4h of this lane's query.
 #pragma unroll
-    for (int bit = 0; bit < 2; bit++)  // channel bits 0,1: v bits 0,1
+    for (int bit = 0; bit < 4; bit++) {  // channel bits 0,1 (v bits 0,1) and 3,4 (v bits 2,3)
 #pragma unroll
       for (int c = 0; c < CBLK; c++)
 #pragma unroll
@@ -419,6 +550,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
             acc[c][v] = a + b;
             acc[c][v | (1 << bit)] = a - b;
           }
+    }
 #pragma unroll
     for (int c = 0; c < CBLK; c++)  // channel bit 2: the partner lane
 #pragma unroll
@@ -426,17 +558,6 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         const float pv = xor32(acc[c][v]);
         acc[c][v] = h ? (pv - acc[c][v]) : (acc[c][v] + pv);
       }
-#pragma unroll
-    for (int bit = 2; bit < 4; bit++)  // channel bits 3,4: v bits 2,3
-#pragma unroll
-      for (int c = 0; c < CBLK; c++)
-#pragma unroll
-        for (int v = 0; v < 16; v++)
-          if ((v & (1 << bit)) == 0) {
-            const float a = acc[c][v], b = acc[c][v | (1 << bit)];
-            acc[c][v] = a + b;
-            acc[c][v | (1 << bit)] = a - b;
-          }
 #pragma unroll
     for (int cb = 1; cb < CBLK; cb <<= 1)  // channel bits 5, 6: the 32-channel block
 #pragma unroll
@@ -462,7 +583,8 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       const uint16_t* qrow = p.q + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h;
 #pragma unroll
       for (int t = 0; t < D / 16; t++) {
-        const uint4 w = q_ok ? reinterpret_cast<const uint4*>(qrow)[t] : make_uint4(0, 0, 0, 0);
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (q_ok) w = reinterpret_cast<const uint4*>(qrow)[t];
         qb16[t] = __builtin_bit_cast(bf16x8, w);
       }
     }
@@ -470,63 +592,75 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     const uint16_t* kr_base = p.k_cur + (size_t)bh * p.n_r * D;
     const uint16_t* vr_base = p.v_cur + (size_t)bh * p.n_r * D;
     const int n_rt = (p.n_r + kBN - 1) / kBN;
-    for (int T = 0; T < n_rt; T++) {
+    constexpr int SEGS = D / 8;              // 16-byte segments per row
+    constexpr int ITEMS = (kBN / 2) * SEGS;  // (token pair, segment) items per tile
+    static_assert(ITEMS <= kThreads, "one staging item per thread");
+    // thread item: tokens (16g + j, 16g + j + 8) -- adjacent value positions -- and one segment
+    const int seg = tid % SEGS, pr = tid / SEGS;
+    const int tokA = 16 * (pr >> 3) + (pr & 7), tokB = tokA + 8;
+    uint4 rka = make_uint4(0, 0, 0, 0), rkb = rka, rva = rka, rvb = rka;
+    auto load_cur = [&](int T) {
+      if (tid >= ITEMS) return;
       const int t0 = T * kBN;
-      const int nvalid = min(kBN, p.n_r - t0);
-      __syncthreads();
-      for (int e = tid; e < kBN * (D / 8); e += kThreads) {
-        const int tok = e / (D / 8), seg = e % (D / 8);
-        const bool ok = tok < nvalid;
-        const uint4 kw = ok ? reinterpret_cast<const uint4*>(kr_base + (size_t)(t0 + tok) * D)[seg]
-                            : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&sm.kr[tok][8 * seg]) = kw;
-        if (!MASS_ONLY) {
-          const uint4 vw = ok ? reinterpret_cast<const uint4*>(vr_base + (size_t)(t0 + tok) * D)[seg]
-                              : make_uint4(0, 0, 0, 0);
-          const uint32_t ww[4] = {vw.x, vw.y, vw.z, vw.w};
-          // position of token tok in its 16-token group: key j + 8e sits at 2j + e
-          const int g = tok >> 4, in = tok & 15;
-          const int pos = 16 * g + 2 * (in & 7) + (in >> 3);
+      const bool okA = t0 + tokA < p.n_r, okB = t0 + tokB < p.n_r;
+      rka = rkb = rva = rvb = make_uint4(0, 0, 0, 0);
+      if (okA) {
+        rka = reinterpret_cast<const uint4*>(kr_base + (size_t)(t0 + tokA) * D)[seg];
+        if (!MASS_ONLY) rva = reinterpret_cast<const uint4*>(vr_base + (size_t)(t0 + tokA) * D)[seg];
+      }
+      if (okB) {
+        rkb = reinterpret_cast<const uint4*>(kr_base + (size_t)(t0 + tokB) * D)[seg];
+        if (!MASS_ONLY) rvb = reinterpret_cast<const uint4*>(vr_base + (size_t)(t0 + tokB) * D)[seg];
+      }
+    };
+    auto store_cur = [&](int T, TileBuf<D, BITS>& tb) {
+      if (tid < kBN) {
+        const int nvalid = min(kBN, p.n_r - T * kBN);
+        tb.mask[32 * (tid >> 5) + key_mrow(tid & 31)] = tid < nvalid ? 0.f : -INFINITY;
+      }
+      if (tid >= ITEMS) return;
+      *reinterpret_cast<uint4*>(&tb.kr[tokA][8 * seg]) = rka;
+      *reinterpret_cast<uint4*>(&tb.kr[tokB][8 * seg]) = rkb;
+      if (!MASS_ONLY) {
+        const uint32_t wa[4] = {rva.x, rva.y, rva.z, rva.w}, wb[4] = {rvb.x, rvb.y, rvb.z, rvb.w};
+        const int pos = 16 * (pr >> 3) + 2 * (pr & 7);  // positions of tokA, tokB: pos, pos + 1
 #pragma unroll
-          for (int e2 = 0; e2 < 4; e2++) {
-            sm.v[8 * seg + 2 * e2][pos] = (_Float16)__uint_as_float(ww[e2] << 16);
-            sm.v[8 * seg + 2 * e2 + 1][pos] = (_Float16)__uint_as_float(ww[e2] & 0xFFFF0000u);
-          }
+        for (int e = 0; e < 4; e++) {
+          const float a0 = __uint_as_float(wa[e] << 16), a1 = __uint_as_float(wa[e] & 0xFFFF0000u);
+          const float b0 = __uint_as_float(wb[e] << 16), b1 = __uint_as_float(wb[e] & 0xFFFF0000u);
+          *reinterpret_cast<uint32_t*>(&tb.v[8 * seg + 2 * e][pos]) = pack_f16x2(a0, b0);
+          *reinterpret_cast<uint32_t*>(&tb.v[8 * seg + 2 * e + 1][pos]) = pack_f16x2(a1, b1);
         }
       }
-      if (tid < kBN) {
-        const int j = tid;
-        sm.mask[32 * (j >> 5) + key_mrow(j & 31)] = j < nvalid ? 0.f : -INFINITY;
-      }
-      __syncthreads();
+    };
+    auto compute_cur = [&](int T, const TileBuf<D, BITS>& tb) {
+      const int nvalid = min(kBN, p.n_r - T * kBN);
       f32x16 sc[2];
 #pragma unroll
       for (int mb = 0; mb < 2; mb++) {
         const int key = 32 * mb + mrow_key(col);
 #pragma unroll
-        for (int v = 0; v < 16; v++) sc[mb][v] = 0.f;
-#pragma unroll
         for (int t = 0; t < D / 16; t++) {
-          const bf16x8 aop = *reinterpret_cast<const bf16x8*>(&sm.kr[key][HALF * h + 8 * t]);
-          sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb16[t], sc[mb], 0, 0, 0);
+          const bf16x8 aop = *reinterpret_cast<const bf16x8*>(&tb.kr[key][HALF * h + 8 * t]);
+          if (t == 0) {
+            const f32x16 z = {};
+            sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb16[t], z, 0, 0, 0);
+          } else {
+            sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb16[t], sc[mb], 0, 0, 0);
+          }
         }
       }
-      float x[2][16];
+      float slv[2][16];
 #pragma unroll
       for (int mb = 0; mb < 2; mb++)
 #pragma unroll
-        for (int v = 0; v < 16; v++) x[mb][v] = sc[mb][v] * sl;
-      if (nvalid < kBN) {
-#pragma unroll
-        for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-          for (int v = 0; v < 16; v++) x[mb][v] += sm.mask[32 * mb + (v & 3) + 8 * (v >> 2) + 4 * h];
-      }
-      softmax_tile(x);
+        for (int v = 0; v < 16; v++) slv[mb][v] = sl;
+      float pv[2][16];
+      softmax_tile(sc, slv, nvalid < kBN, tb.mask, pv);
 #pragma unroll
       for (int mb = 0; mb < 2; mb++)
 #pragma unroll
-        for (int v = 0; v < 16; v++) l_r += x[mb][v];
+        for (int v = 0; v < 16; v++) l_r += pv[mb][v];
       if (!MASS_ONLY) {
         uint32_t pb[4][4];
 #pragma unroll
@@ -535,11 +669,21 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
           for (int v4 = 0; v4 < 4; v4++) {
             const int v = 4 * v4;
             const int ks = 2 * mb + (v4 >> 1), slot = 2 * (v4 & 1);
-            pb[ks][slot] = pack_f16x2(x[mb][v], x[mb][v + 1]);
-            pb[ks][slot + 1] = pack_f16x2(x[mb][v + 2], x[mb][v + 3]);
+            pb[ks][slot] = pack_f16x2(pv[mb][v], pv[mb][v + 1]);
+            pb[ks][slot + 1] = pack_f16x2(pv[mb][v + 2], pv[mb][v + 3]);
           }
-        pv_tile(pb);
+        pv_tile(tb, pb);
       }
+    };
+    load_cur(0);
+    store_cur(0, sm.buf[0]);
+    __syncthreads();
+    for (int T = 0; T < n_rt; T++) {
+      const bool has_next = T + 1 < n_rt;
+      if (has_next) load_cur(T + 1);
+      compute_cur(T, sm.buf[T & 1]);
+      if (has_next) store_cur(T + 1, sm.buf[(T + 1) & 1]);
+      __syncthreads();
     }
   }
 

@@ -9,33 +9,39 @@
 // Taylor form s^2 sum_c q'_c^2 Delta_c^2 / 24 of that inflation (per token:
 // s^2 |q|^2 Delta_j^2 / 24).
 //
-// Kernel design (one workgroup = 8 waves = 256 queries of one head; a wave owns 32
-// queries and streams 64-key tiles through a two-stage LDS pipeline, one barrier per
-// tile, the next tile's global loads in flight during the current tile's math):
-//  * Scores are computed transposed, S^T = K Q^T, so keys are the MFMA M dimension and
-//    each lane owns one query: per-query softmax state lives in one lane (and its
-//    partner lane l^32, which holds the other half of each key block).
-//  * Cached QK^T runs on int8 MFMA (v_mfma_i32_32x32x32_i8): the rotated query
-//    q' = H q is a 16-bit fixed-point integer (scale sigma) split into signed hi/lo
-//    bytes, the key operand is the raw 2- or 4-bit code, unpacked in registers with
-//    shifts and masks; integer accumulation is exact: S = 256 S_hi + S_lo.
-//  * The zero point and the correction enter through one fp16 MFMA per 32x32 block whose
-//    key operand is (z_j, z_j, Delta_j, Delta_j) and whose query operand is the hi/lo
-//    fp16 split of (-A sum(q_fixed), -G): bias_ij = -A z_j sum(q_fixed) - G Delta_j.
-//    Logit in log2 units: x = Delta_j (A S + bias), A = s sigma log2 e,
-//    G = s^2 |q'|^2 / 24 log2 e.
-//  * Softmax with a lazy running max m: p = exp2(Delta_j * inner - m) in one fma and one
-//    exp; the exact max and the rescale run only when a tile's p exceeds 2^8 (or for a
-//    ragged tile), so P values stay below 2^8 and in fp16 range.
-//  * PV runs on fp16 MFMA: P~ = p Delta^V_j rounded to fp16, times (code - z) exact in
-//    fp16, unpacked once per workgroup into LDS (channel-major rows). A fixed key
-//    permutation inside each 32-key block lets P~ feed the B operand straight from the
-//    score registers.
-//  * The cached PV sum lives in the rotated basis; it is un-rotated once (an FWHT across
-//    the accumulator registers) before the current chunk is processed with bf16 QK^T
-//    and fp16 PV. One online softmax (shared running max, separate sums l_S, l_R)
-//    covers both phases.
+// Kernel design. A workgroup is 8 waves (two per SIMD) and 256 queries of one head; a
+// wave owns 32 queries and walks 32-key blocks (two per 64-key tile), first over the
+// cached window, then over the current chunk.
+//  * Scores are computed transposed, S^T = K Q^T: keys are the MFMA M dimension and
+//    each lane owns one query (lane l^32 holds the other half of every 32-key block),
+//    so the softmax state of a query lives in one lane pair.
+//  * Cached QK^T runs on int8 MFMA (v_mfma_i32_32x32x32_i8). The rotated query
+//    q' = H q is a 16-bit fixed-point integer q_f (one scale sigma per wave) split into
+//    signed bytes q_f = 256 hi + lo; the key operand is the raw code, unpacked once per
+//    workgroup into LDS; S = 256 S_hi + S_lo is exact in int32.
+//  * The zero point, the correction, the reference max and the padding mask enter
+//    through one fp16 MFMA per block whose key operand holds Delta_j z_j, Delta_j^2
+//    (hi/lo fp16 pairs), 1 and the mask, and whose query operand holds -A sum(q_f),
+//    -G, -m and a large negative constant. In log2 units the logit is
+//    x = (Delta_j A) S + c with A = s sigma log2 e and G = s^2 |q'|^2 / 24 log2 e, so a
+//    score costs a shift-add, a convert, one fma and one exp2.
+//  * The reference max m is fixed for a whole pass over the keys: the first block's
+//    maximum plus a headroom of 2^8. p = exp2(x) then needs no rescaling of the
+//    accumulator; a block whose fp16 row sum passes 2^15 records a bound of its maximum
+//    and the workgroup repeats the pass with the raised m (rare; bounded).
+//  * PV on fp16 MFMA: P = fp16(p) straight from the score registers (a fixed key
+//    permutation inside each 32-key block makes the score layout the B operand); the
+//    value tile in LDS holds fp16((code - z) Delta^V), exact in the subtraction. The
+//    sums l_S, l_R add the same fp16 P.
+//  * The cached PV sum is in the rotated basis and is un-rotated once (an FWHT across
+//    the accumulator registers) before the current chunk, which runs on bf16 QK^T
+//    (exact products) and fp16 PV.
+//  * Keys and per-key parameters are staged two tiles ahead, values one tile ahead
+//    (a three-slot LDS ring), by all eight waves, with one barrier per tile; the two
+//    waves of a SIMD overlap each other's matrix-core and VALU work.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -51,11 +57,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // queries per workgroup
-constexpr int kBN = 64;           // keys per tile
+constexpr int kStreams = 1;             // 32-query streams per wave
+constexpr int kNS = kWaves * kStreams;  // streams per workgroup
+constexpr int kBM = 32 * kNS;           // queries per workgroup
+constexpr int kBN = 64;                 // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kQFix = 32639.f;  // |q_fixed| <= 32639 keeps hi = (q+128)>>8 in int8
-constexpr float kLazy = 256.f;    // 2^8: largest p allowed before the running max is raised
+constexpr float kPmax = 32768.f;     // largest fp16 row sum of a block accepted in a pass
+constexpr float kHeadroom = 8.f;     // first reference max: the first block's max + 8 (log2 units)
+constexpr float kRaise = 24.f;       // largest raise of the reference max per restart (log2 units)
+constexpr int kMaxPasses = 8;        // passes over the keys (restarts are rare; see the softmax)
+constexpr float kMaskLogit = 65504.f;  // subtracted from padded keys' logits (log2 units)
+constexpr float kD2Scale = 64.f;     // Delta^2 is carried as Delta^2 / 64 (fp16 range)
+
+constexpr float kQFix = 32639.f;  // |q_f| <= 32639 keeps hi = (q_f + 128) >> 8 in int8
 
 struct Params {
   int B, H, n_q, n_r, chunk_len, n_chunks, cp;
@@ -104,6 +118,12 @@ __device__ inline uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// fp16 hi/lo split of x: hi = fp16(x), lo = fp16(x - hi).
+__device__ inline void split16(float x, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)(x - (float)hi);
+}
+
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32); }
 __device__ inline float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -120,36 +140,62 @@ __device__ inline void xcd_map(int L, int total, int n_qblk, int& qb, int& bh) {
   bh = w / n_qblk;
 }
 
-template <int D, int BITS>
-struct TileBuf {
-  static constexpr int KW = D * BITS / 32;  // key words per token
-  static constexpr int VROW = kBN + 8;      // fp16 per value row (padded against bank conflicts)
-  alignas(16) uint32_t k_words[kBN][KW];    // cached keys, natural token order
-  alignas(16) _Float16 v[D][VROW];          // (code - z) or current-chunk values, channel-major
-  alignas(16) uint16_t kr[kBN][D + 8];      // current-chunk keys (bf16), natural order
-  alignas(16) float dk[kBN];                // per key, M-row order
-  alignas(16) float dv[kBN];
-  alignas(16) float mask[kBN];
-  alignas(16) uint2 kb[kBN];                // bias operand: (z, z), (Delta, Delta) as fp16
+template <int D>
+struct Smem {
+  static constexpr int VROW = kBN + 8;  // fp16 per value row (padded against bank conflicts)
+  static constexpr int KROW = D + 16;   // bytes per unpacked key row
+  union KSlot {
+    uint8_t c[kBN][KROW];     // cached key codes (kperm order per 16 channels)
+    uint16_t kr[kBN][D + 8];  // current-chunk keys (bf16), natural order
+  };
+  struct PSlot {
+    float dka[kNS][kBN];  // Delta_j A of each stream (cached; 0 for padding), M-row order
+    uint4 kb[kBN][2];     // bias operand rows (16 fp16), M-row order
+  };
+  struct ZSlot {
+    uint32_t zv[kBN / 2];   // (-1024 - z^V) fp16 pairs, token pair (j, j+8) order
+    uint32_t dvp[kBN / 2];  // (Delta^V_j, Delta^V_j+8) fp16 pairs
+  };
+  alignas(16) KSlot k[3];
+  alignas(16) _Float16 v[3][D][VROW];  // value rows: fp16((code - z) Delta^V) or current values
+  alignas(16) PSlot prm[3];
+  alignas(16) ZSlot z[3];
+  alignas(16) float a_stream[kNS];
+  int fail;
 };
 
-template <int D, int BITS>
-struct Smem {
-  TileBuf<D, BITS> buf[2];
-  alignas(16) uint32_t zv_pair[2][kBN / 2];  // (-1024 - z) fp16 pairs of a tile's value tokens
-};
+#define KVQ_INLINE __attribute__((always_inline))
+
+enum : int { kNone = 0, kCached = 1, kCurrent = 2 };
+template <int K>
+using Kind = std::integral_constant<int, K>;
 
 template <int D, int BITS, bool MASS_ONLY>
 __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
+  using SM = Smem<D>;
   constexpr int HALF = D / 2;
   constexpr int KSTEPS = D / 32;  // int8 K-steps of 32 channels
   constexpr int CBLK = D / 32;    // 32-channel output blocks
   constexpr int CPW = 32 / BITS;
-  constexpr int KW = D * BITS / 32;    // key words per token
-  constexpr int VWPC = kBN / CPW;      // value words per channel per 64-token block
-  constexpr int KWT = kBN * KW;        // key words per tile
-  constexpr int VWT = D * VWPC;        // value words per tile
-  __shared__ Smem<D, BITS> sm;
+  constexpr int KW = D * BITS / 32;  // key words per token
+  constexpr int VWPC = kBN / CPW;    // value words per channel per 64-token block
+  constexpr int VWT = D * VWPC;      // value words per tile
+  constexpr int KU = BITS / 2;       // key words per 16-channel unit
+  constexpr int KUNITS = kBN * D / 16;
+  constexpr int WPG = BITS / 2;             // value words per 16-token group
+  constexpr int VGROUPS = D * (kBN / 16);   // 16-token value groups per tile
+  constexpr int SEGS = D / 8;               // 16-byte segments of a bf16 row
+  constexpr int RITEMS = kBN * SEGS;        // current-key (token, segment) items per tile
+  constexpr int VITEMS = (kBN / 2) * SEGS;  // current-value (token pair, segment) items per tile
+  // items per thread (work counts below kThreads leave whole waves idle)
+  constexpr int KUPT = (KUNITS + kThreads - 1) / kThreads;
+  constexpr int VGPT = (VGROUPS + kThreads - 1) / kThreads;
+  constexpr int RIPT = (RITEMS + kThreads - 1) / kThreads;
+  constexpr int VRPT = (VITEMS + kThreads - 1) / kThreads;
+  static_assert(kStreams == 1, "one 32-query stream per wave");
+  static_assert(KUNITS % 64 == 0 && VGROUPS % 64 == 0 && RITEMS % 64 == 0 && VITEMS % 64 == 0, "wave-uniform split");
+  static_assert(KUPT <= RIPT && VGPT <= 2 * VRPT && RIPT <= 4 && VRPT <= 2, "staging registers");
+  __shared__ SM sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -158,12 +204,14 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   xcd_map(blockIdx.x, gridDim.x, p.n_qblk, qb, bh);
   const int qi = qb * kBM + wave * 32 + col;  // this lane's query
   const bool q_ok = qi < p.n_q;
+  const float sl = p.s * kLog2e;
 
-  // ---------------- prologue: rotated query as 16-bit fixed point, hi/lo bytes --------
-  i32x4 qhi[KSTEPS], qlo[KSTEPS];
-  f16x8 qbias;  // B operand of the bias MFMA
-  float A;
-  {
+  // ---------------- query operands ----------------
+  i32x4 qhi[KSTEPS], qlo[KSTEPS];  // int8 hi/lo of q_f (cached keys), or the bf16 query
+  f16x8 qbias;                     // query operand of the bias MFMA
+  float m_run = -INFINITY;         // reference max (log2 units); -inf until the first block
+  float a_st = 0.f;                // A of this wave's stream
+  auto build_query = [&]() KVQ_INLINE {
     float qv[HALF];
     const uint16_t* qrow = p.q + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h;
 #pragma unroll
@@ -201,9 +249,10 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       mxa = fmaxf(mxa, fabsf(qv[i]));
     }
     ss += xor32(ss);
-    mxa = fmaxf(mxa, xor32(mxa));
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));  // stream-wide max
     const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
-    const float sigma = mxa > 0.f ? mxa / kQFix : 0.f;
+    const float A = mxa > 0.f ? sl * (mxa / kQFix) : 0.f;
     int qs = 0;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; kk++)
@@ -223,73 +272,66 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         qlo[kk][j] = (int)wlo;
       }
     qs += __shfl_xor(qs, 32);
-    A = p.s * sigma * kLog2e;
     const float G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
-    // bias = z_j * (-A qs) + Delta_j * (-G), each factor split into fp16 hi + lo
-    const float bz = -A * (float)qs, bd = -G;
-    const _Float16 bz_hi = (_Float16)bz, bd_hi = (_Float16)bd;
-    const _Float16 bz_lo = (_Float16)(bz - (float)bz_hi), bd_lo = (_Float16)(bd - (float)bd_hi);
-#pragma unroll
-    for (int e = 0; e < 8; e++) qbias[e] = (_Float16)0.f;
+    // query-side factors of the bias MFMA (key side in the tile parameters):
+    //   (Delta_j z_j) * w + (Delta_j^2 / 64) * g - m - 65504 * mask_j
+    const float w = -A * (float)qs;
+    const float g = -G * kD2Scale;
+    _Float16 wh, wl, gh, gl;
+    split16(w, wh, wl);
+    split16(g, gh, gl);
     if (h == 0) {
-      qbias[0] = bz_hi;
-      qbias[1] = bz_lo;
-      qbias[2] = bd_hi;
-      qbias[3] = bd_lo;
+      qbias[0] = wh;
+      qbias[1] = wl;
+      qbias[2] = wh;
+      qbias[3] = gh;
+      qbias[4] = gl;
+      qbias[5] = gh;
+      qbias[6] = (_Float16)0.f;
+      qbias[7] = (_Float16)0.f;
+    } else {
+      // -m (hi, lo); 0 while m is unset
+      _Float16 mh = (_Float16)0.f, ml = (_Float16)0.f;
+      if (m_run != -INFINITY) split16(-m_run, mh, ml);
+      qbias[0] = mh;
+      qbias[1] = ml;
+      qbias[2] = (_Float16)(-kMaskLogit);
+#pragma unroll
+      for (int e = 3; e < 8; e++) qbias[e] = (_Float16)0.f;
     }
-  }
-
-  float m_run = -INFINITY, l_s = 0.f, l_r = 0.f;
-  f32x16 acc[CBLK];
-#pragma unroll
-  for (int c = 0; c < CBLK; c++)
-#pragma unroll
-    for (int v = 0; v < 16; v++) acc[c][v] = 0.f;
-
-  // Exact max + rescale for a tile whose logits x (log2 units, masked) are given; the
-  // returned x hold p = exp2(x - m_run).
-  auto exact_tile = [&](float (&x)[2][16]) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-      for (int v = 0; v < 16; v++) mx = fmaxf(mx, x[mb][v]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    if (__ballot(m_new > m_run) != 0) {
-      const float sc = exp2_(m_run - m_new);
-      l_s *= sc;
-      l_r *= sc;
-      if (!MASS_ONLY) {
-#pragma unroll
-        for (int c = 0; c < CBLK; c++)
-#pragma unroll
-          for (int v = 0; v < 16; v++) acc[c][v] *= sc;
-      }
-      m_run = m_new;
-    }
-#pragma unroll
-    for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-      for (int v = 0; v < 16; v++) x[mb][v] = exp2_(x[mb][v] - m_run);
+    if (lane == 0) sm.a_stream[wave] = A;
+    __syncthreads();
+    a_st = sm.a_stream[wave];
   };
-
-  // PV for one tile: B operand = P (fp16 pairs from the score registers), A = value rows in LDS.
-  auto pv_tile = [&](const TileBuf<D, BITS>& tb, const uint32_t (&pb)[4][4]) {
+  // From the first current-chunk tile on, the int8 query operands are no longer needed;
+  // their registers take the bf16 query (half h: channels HALF h .. HALF h + HALF - 1).
+  auto load_query_bf16 = [&]() KVQ_INLINE {
+    const uint4* qrow16 = reinterpret_cast<const uint4*>(p.q + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h);
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-      const f16x8 bop = __builtin_bit_cast(f16x8, make_uint4(pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]));
-#pragma unroll
-      for (int c = 0; c < CBLK; c++) {
-        const f16x8 aop = *reinterpret_cast<const f16x8*>(&tb.v[32 * c + col][16 * ks + 8 * h]);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, acc[c], 0, 0, 0);
-      }
+    for (int t = 0; t < D / 16; t++) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (q_ok) w = qrow16[t];
+      if (t < KSTEPS)
+        qhi[t] = __builtin_bit_cast(i32x4, w);
+      else
+        qlo[t - KSTEPS] = __builtin_bit_cast(i32x4, w);
     }
   };
+  // Sets the reference max to mx, rounded to what the bias operand carries (-m as an
+  // fp16 hi + lo pair in query slots 8, 9).
+  auto set_m = [&](float mx) KVQ_INLINE {
+    _Float16 mh, ml;
+    split16(-mx, mh, ml);
+    m_run = -((float)mh + (float)ml);
+    qbias[0] = h ? mh : qbias[0];
+    qbias[1] = h ? ml : qbias[1];
+  };
+  build_query();
 
-  // ---------------- phase 1: cached window ----------------
+  // ---------------- tile geometry ----------------
   const int tiles_per_chunk = p.cp / kBN;
-  const int n_tiles = p.n_chunks * tiles_per_chunk;
+  const int n_ct = p.n_chunks * tiles_per_chunk;  // cached tiles
+  const int n_rt = (p.n_r + kBN - 1) / kBN;       // current-chunk tiles
   const size_t n_tot = (size_t)p.n_chunks * p.cp;
   const uint32_t* kc_base = p.k_codes + (size_t)bh * n_tot * KW;
   const uint32_t* vc_base = p.v_codes + (size_t)bh * (n_tot / kBN) * VWT;
@@ -297,247 +339,357 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   const uint16_t* kz_base = p.k_zero + (size_t)bh * n_tot;
   const uint16_t* vs_base = p.v_scale + (size_t)bh * n_tot;
   const uint16_t* vz_base = p.v_zero + (size_t)bh * n_tot;
-
-
-  // ---- prefetch registers: key words, one 16-token group of value words, per-key fp16 ----
-  constexpr int KPT = KWT >= kThreads ? KWT / kThreads : 1;  // key words per thread (contiguous)
-  constexpr int WPG = BITS / 2;                                // value words per 16-token group
-  constexpr int VGT = D * (kBN / 16);                          // value groups per tile (<= kThreads)
-  static_assert(KWT <= 2 * kThreads && VGT <= kThreads, "tile staging assumes at most 2 words per thread");
-  uint32_t kwr[KPT], vwr[WPG];
-  uint32_t pk_dk = 0, pk_zk = 0, pk_dv = 0;  // per-key fp16 bits (threads < kBN)
-  uint32_t pz0 = 0, pz1 = 0;                 // value zero points of a token pair (threads < kBN/2)
-#pragma unroll
-  for (int e = 0; e < KPT; e++) kwr[e] = 0;
-#pragma unroll
-  for (int e = 0; e < WPG; e++) vwr[e] = 0;
-
-  auto load_tile = [&](int T) {
-    const size_t tok0 = (size_t)T * kBN;
-    if (tid * KPT < KWT) {
-      const uint32_t* src = kc_base + tok0 * KW + tid * KPT;
-      if constexpr (KPT == 2) {
-        const uint2 w = *reinterpret_cast<const uint2*>(src);
-        kwr[0] = w.x;
-        kwr[KPT - 1] = w.y;
-      } else {
-        kwr[0] = src[0];
-      }
-    }
-    if (!MASS_ONLY && tid < VGT) {
-      const uint32_t* src = vc_base + (size_t)T * VWT + tid * WPG;
-      if constexpr (WPG == 2) {
-        const uint2 w = *reinterpret_cast<const uint2*>(src);
-        vwr[0] = w.x;
-        vwr[WPG - 1] = w.y;
-      } else {
-        vwr[0] = src[0];
-      }
-    }
-    if (tid < kBN) {
-      pk_dk = ks_base[tok0 + tid];
-      pk_zk = kz_base[tok0 + tid];
-      if (!MASS_ONLY) pk_dv = vs_base[tok0 + tid];
-    }
+  const uint16_t* kr_base = p.k_cur + (size_t)bh * p.n_r * D;
+  const uint16_t* vr_base = p.v_cur + (size_t)bh * p.n_r * D;
+  auto n_valid = [&](int U) KVQ_INLINE {
+    return U < n_ct ? min(kBN, p.chunk_len - (U % tiles_per_chunk) * kBN) : min(kBN, p.n_r - (U - n_ct) * kBN);
   };
-  auto load_zv = [&](int T) {
-    if (!MASS_ONLY && tid < kBN / 2) {
-      const size_t tok0 = (size_t)T * kBN;
-      const int g = tid >> 3, j = tid & 7;
-      pz0 = vz_base[tok0 + 16 * g + j];
-      pz1 = vz_base[tok0 + 16 * g + j + 8];
-    }
-  };
-  auto store_zv = [&](int slot) {
-    if (!MASS_ONLY && tid < kBN / 2)
-      sm.zv_pair[slot][tid] = pack_f16x2(-1024.f - half_bits_to_f32(pz0), -1024.f - half_bits_to_f32(pz1));
-  };
-  // Key words, per-key values and the unpacked value tile of tile T (its zero-point
-  // pairs must already be visible in zv_pair[T & 1]).
-  auto store_tile = [&](int T, TileBuf<D, BITS>& tb) {
-    if (tid * KPT < KWT) {
-      uint32_t* dst = &tb.k_words[0][0] + tid * KPT;
-      if constexpr (KPT == 2)
-        *reinterpret_cast<uint2*>(dst) = make_uint2(kwr[0], kwr[KPT - 1]);
-      else
-        dst[0] = kwr[0];
-    }
-    if (tid < kBN) {
-      const int r = 32 * (tid >> 5) + key_mrow(tid & 31);
-      const int nvalid = min(kBN, p.chunk_len - (T % tiles_per_chunk) * kBN);
-      tb.dk[r] = half_bits_to_f32(pk_dk);
-      tb.dv[r] = half_bits_to_f32(pk_dv);
-      tb.mask[r] = tid < nvalid ? 0.f : -INFINITY;
-      tb.kb[r] = make_uint2((pk_zk & 0xFFFFu) | (pk_zk << 16), (pk_dk & 0xFFFFu) | (pk_dk << 16));
-    }
-    if (!MASS_ONLY && tid < VGT) {
-      const int ch = tid >> 2, g = tid & 3;  // 16-token group g of channel ch
-      const uint4* zp = reinterpret_cast<const uint4*>(&sm.zv_pair[T & 1][8 * g]);
-      const uint4 z0 = zp[0], z1 = zp[1];
-      const uint32_t zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-      uint32_t a[8];
-      if constexpr (BITS == 2) {
-        const uint32_t w = vwr[0];
+
+  // ---------------- staging (all threads) ----------------
+  // Step T stages the keys, per-key parameters and value zero-point / step pairs of
+  // tile T+2, and the values of tile T+1. Global loads are issued at the start of the
+  // step, unconditional, with indices clamped into the arrays (positions past the end
+  // are replaced when stored); the LDS stores come at its end, before the barrier.
+  uint4 kpre[RIPT];          // keys (code units, or current rows)
+  uint4 vpre[2 * VRPT];      // values (code groups, or current row pairs)
+  uint32_t pk_dk = 0, pk_zk = 0;                 // key step / zero point of key tid & 63
+  uint32_t pz0 = 0, pz1 = 0, pd0 = 0, pd1 = 0;   // value zero points / steps of a token pair
+
+  auto load_k = [&](int U, auto k_c) KVQ_INLINE {
+    if constexpr (decltype(k_c)::value == kCached) {
+      const size_t tok0 = (size_t)U * kBN;
 #pragma unroll
-        for (int j = 0; j < 8; j++) a[j] = ((w >> (2 * j)) & 0x00030003u) | 0x64006400u;
-      } else {
-        // t0 = [w0.b0 w0.b1 w1.b0 w1.b1], t1 = [w0.b2 w0.b3 w1.b2 w1.b3]
-        const uint32_t w0 = vwr[0], w1 = vwr[WPG - 1];
-        const uint32_t t0 = (w0 & 0xFFFFu) | (w1 << 16);
-        const uint32_t t1 = (w0 >> 16) | (w1 & 0xFFFF0000u);
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          a[j] = ((t0 >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-          a[4 + j] = ((t1 >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+      for (int i = 0; i < KUPT; i++) {
+        const int un = min(tid + i * kThreads, KUNITS - 1);
+        const uint32_t* src = kc_base + tok0 * KW + (size_t)un * KU;
+        if constexpr (KU == 2) {
+          const uint2 w = *reinterpret_cast<const uint2*>(src);
+          kpre[i].x = w.x;
+          kpre[i].y = w.y;
+        } else {
+          kpre[i].x = src[0];
         }
       }
-      uint32_t res[8];
-#pragma unroll
-      for (int j = 0; j < 8; j++)
-        res[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a[j]) + __builtin_bit_cast(f16x2, zz[j]));
-      uint4* dst = reinterpret_cast<uint4*>(&tb.v[ch][16 * g]);
-      dst[0] = make_uint4(res[0], res[1], res[2], res[3]);
-      dst[1] = make_uint4(res[4], res[5], res[6], res[7]);
-    }
-  };
-
-  // Lazy softmax over one tile: inner scores are turned into p = exp2(scale*inner - m)
-  // by one fma and one exp when that keeps every p <= 2^8; otherwise (and for ragged
-  // tiles, which need the mask) the exact max path runs. scl[mb][v] multiplies inner.
-  auto softmax_tile = [&](const f32x16 (&inner)[2], const float (&scl)[2][16], bool ragged,
-                          const float* mask_rows, float (&pv)[2][16]) {
-    bool fast = !ragged;
-    if (fast) {
-      float pmax = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-        for (int v = 0; v < 16; v++) {
-          pv[mb][v] = exp2_(fmaf(scl[mb][v], inner[mb][v], -m_run));
-          pmax = fmaxf(pmax, pv[mb][v]);
-        }
-      pmax = fmaxf(pmax, xor32(pmax));
-      fast = __ballot(!(pmax <= kLazy)) == 0;
-    }
-    if (!fast) {
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-        for (int v = 0; v < 16; v++) {
-          pv[mb][v] = scl[mb][v] * inner[mb][v];
-          if (ragged) pv[mb][v] += mask_rows[32 * mb + (v & 3) + 8 * (v >> 2) + 4 * h];
-        }
-      exact_tile(pv);
-    }
-  };
-
-  auto compute_cached = [&](int T, const TileBuf<D, BITS>& tb) {
-    const int nvalid = min(kBN, p.chunk_len - (T % tiles_per_chunk) * kBN);
-    i32x16 shi[2], slo[2];
-    f32x16 inner[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; mb++) {
-      const int key = 32 * mb + mrow_key(col);
-      uint32_t kw[KW / 2];
-      if constexpr (KW / 2 == 4) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&tb.k_words[key][(KW / 2) * h]);
-        kw[0] = w.x; kw[1] = w.y; kw[2] = w.z; kw[3] = w.w;
-      } else if constexpr (KW / 2 == 8) {
-        const uint4 w0 = *reinterpret_cast<const uint4*>(&tb.k_words[key][(KW / 2) * h]);
-        const uint4 w1 = *reinterpret_cast<const uint4*>(&tb.k_words[key][(KW / 2) * h + 4]);
-        kw[0] = w0.x; kw[1] = w0.y; kw[2] = w0.z; kw[3] = w0.w;
-        kw[4 % (KW / 2)] = w1.x; kw[5 % (KW / 2)] = w1.y; kw[6 % (KW / 2)] = w1.z; kw[7 % (KW / 2)] = w1.w;
-      } else {
-        const uint2 w = *reinterpret_cast<const uint2*>(&tb.k_words[key][(KW / 2) * h]);
-        kw[0] = w.x; kw[1 % (KW / 2)] = w.y;
+      pk_dk = ks_base[tok0 + (tid & (kBN - 1))];
+      pk_zk = kz_base[tok0 + (tid & (kBN - 1))];
+      if constexpr (!MASS_ONLY) {
+        const int g = (tid >> 3) & 3, j = tid & 7;
+        pz0 = vz_base[tok0 + 16 * g + j];
+        pz1 = vz_base[tok0 + 16 * g + j + 8];
+        pd0 = vs_base[tok0 + 16 * g + j];
+        pd1 = vs_base[tok0 + 16 * g + j + 8];
       }
+    } else {
+      const int t0 = (U - n_ct) * kBN;
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk++) {
-        i32x4 aop;
+      for (int i = 0; i < RIPT; i++) {
+        const int it = min(tid + i * kThreads, RITEMS - 1);
+        const int tok = min(t0 + it / SEGS, p.n_r - 1), seg = it % SEGS;
+        kpre[i] = reinterpret_cast<const uint4*>(kr_base + (size_t)tok * D)[seg];
+      }
+    }
+  };
+  auto store_k = [&](int U, auto k_c) KVQ_INLINE {
+    typename SM::KSlot& ks = sm.k[U % 3];
+    typename SM::PSlot& ps = sm.prm[U % 3];
+    const int nv = n_valid(U);
+    if constexpr (decltype(k_c)::value == kCached) {
+#pragma unroll
+      for (int i = 0; i < KUPT; i++) {
+        const int un = tid + i * kThreads;
+        if (KUNITS % kThreads != 0 && un >= KUNITS) break;
+        const int tok = un / (D / 16), ui = un % (D / 16);
+        uint4 lo;
         if constexpr (BITS == 2) {
-          const uint32_t w = kw[kk];
-#pragma unroll
-          for (int j = 0; j < 4; j++) aop[j] = (int)((w >> (2 * j)) & 0x03030303u);
+          const uint32_t w = kpre[i].x;
+          lo = make_uint4(w & 0x03030303u, (w >> 2) & 0x03030303u, (w >> 4) & 0x03030303u, (w >> 6) & 0x03030303u);
         } else {
-          const uint32_t w0 = kw[2 * kk], w1 = kw[2 * kk + 1];
-          aop[0] = (int)(w0 & 0x0F0F0F0Fu);
-          aop[1] = (int)((w0 >> 4) & 0x0F0F0F0Fu);
-          aop[2] = (int)(w1 & 0x0F0F0F0Fu);
-          aop[3] = (int)((w1 >> 4) & 0x0F0F0F0Fu);
+          const uint32_t w0 = kpre[i].x, w1 = kpre[i].y;
+          lo = make_uint4(w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu);
         }
-        if (kk == 0) {
-          const i32x16 z = {};
-          shi[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, qhi[kk], z, 0, 0, 0);
-          slo[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, qlo[kk], z, 0, 0, 0);
-        } else {
-          shi[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, qhi[kk], shi[mb], 0, 0, 0);
-          slo[mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, qlo[kk], slo[mb], 0, 0, 0);
+        *reinterpret_cast<uint4*>(&ks.c[tok][16 * ui]) = lo;
+      }
+      // Delta_j A of each wave's stream; 0 for padding keys (their logit is set by the mask)
+      {
+        const int key = tid & (kBN - 1);
+        const int r = 32 * (key >> 5) + key_mrow(key & 31);
+        const float dk = key < nv ? half_bits_to_f32(pk_dk) : 0.f;
+        ps.dka[wave][r] = dk * a_st;
+      }
+      if (wave == 0) {
+        // bias key operand, slots 0..7: dz_hi, dz_hi, dz_lo, d2_hi, d2_hi, d2_lo, 0, 0
+        const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
+        uint4 row = make_uint4(0, 0, 0, 0);
+        if (lane < nv) {
+          const float dk = half_bits_to_f32(pk_dk), zk = half_bits_to_f32(pk_zk);
+          _Float16 dzh, dzl, d2h, d2l;
+          split16(dk * zk, dzh, dzl);
+          split16(dk * dk * (1.f / kD2Scale), d2h, d2l);
+          const uint32_t dzh_b = __builtin_bit_cast(uint16_t, dzh), dzl_b = __builtin_bit_cast(uint16_t, dzl);
+          const uint32_t d2h_b = __builtin_bit_cast(uint16_t, d2h), d2l_b = __builtin_bit_cast(uint16_t, d2l);
+          row.x = dzh_b | (dzh_b << 16);
+          row.y = dzl_b | (d2h_b << 16);
+          row.z = d2h_b | (d2l_b << 16);
+        }
+        ps.kb[r][0] = row;
+      }
+      if constexpr (!MASS_ONLY) {
+        if (wave == 2 && lane < kBN / 2) {
+          typename SM::ZSlot& zs = sm.z[U % 3];
+          const int g = lane >> 3, j = lane & 7;
+          const bool ok0 = 16 * g + j < nv, ok1 = 16 * g + j + 8 < nv;
+          zs.zv[lane] = pack_f16x2(ok0 ? -1024.f - half_bits_to_f32(pz0) : -1024.f,
+                                   ok1 ? -1024.f - half_bits_to_f32(pz1) : -1024.f);
+          zs.dvp[lane] = (ok0 ? (pd0 & 0xFFFFu) : 0u) | ((ok1 ? (pd1 & 0xFFFFu) : 0u) << 16);
         }
       }
-      const uint2 kb = tb.kb[32 * mb + col];
-      const f16x8 bop = __builtin_bit_cast(f16x8, make_uint4(kb.x, kb.y, 0u, 0u));
-      const f32x16 zf = {};
-      inner[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bop, qbias, zf, 0, 0, 0);
+    } else {
+      const int t0 = (U - n_ct) * kBN;
+#pragma unroll
+      for (int i = 0; i < RIPT; i++) {
+        const int it = tid + i * kThreads;
+        if (RITEMS % kThreads != 0 && it >= RITEMS) break;
+        const int tok = it / SEGS, seg = it % SEGS;
+        *reinterpret_cast<uint4*>(&ks.kr[tok][8 * seg]) = t0 + tok < p.n_r ? kpre[i] : make_uint4(0, 0, 0, 0);
+      }
+      if (wave == 0) {
+        const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
+        ps.kb[r][0] = make_uint4(0, 0, 0, 0);
+      }
     }
+    if (wave == 1) {
+      // bias key operand, slots 8..15: 1, 1, mask, 0...
+      const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
+      const uint32_t one = 0x3C00u;
+      ps.kb[r][1] = make_uint4(one | (one << 16), lane < nv ? 0u : one, 0u, 0u);
+    }
+  };
+  auto load_v = [&](int U, auto k_c) KVQ_INLINE {
+    if constexpr (MASS_ONLY) return;
+    if constexpr (decltype(k_c)::value == kCached) {
 #pragma unroll
-    for (int mb = 0; mb < 2; mb++)
+      for (int i = 0; i < VGPT; i++) {
+        const int vg = min(tid + i * kThreads, VGROUPS - 1);
+        const uint32_t* src = vc_base + (size_t)U * VWT + (size_t)vg * WPG;
+        if constexpr (WPG == 2) {
+          const uint2 w = *reinterpret_cast<const uint2*>(src);
+          vpre[i].x = w.x;
+          vpre[i].y = w.y;
+        } else {
+          vpre[i].x = src[0];
+        }
+      }
+    } else {
+      // item (token pair pr, segment seg): tokens 16(pr>>3) + (pr&7) and that + 8
+      const int t0 = (U - n_ct) * kBN;
 #pragma unroll
-      for (int v = 0; v < 16; v++) inner[mb][v] = fmaf(A, (float)((shi[mb][v] << 8) + slo[mb][v]), inner[mb][v]);
-    float dk[2][16];
+      for (int i = 0; i < VRPT; i++) {
+        const int it = min(tid + i * kThreads, VITEMS - 1);
+        const int seg = it % SEGS, pr = it / SEGS;
+        const int tokA = 16 * (pr >> 3) + (pr & 7);
+        vpre[2 * i] = reinterpret_cast<const uint4*>(vr_base + (size_t)min(t0 + tokA, p.n_r - 1) * D)[seg];
+        vpre[2 * i + 1] = reinterpret_cast<const uint4*>(vr_base + (size_t)min(t0 + tokA + 8, p.n_r - 1) * D)[seg];
+      }
+    }
+  };
+  auto store_v = [&](int U, auto k_c) KVQ_INLINE {  // the pairs of tile U must be visible in sm.z[U % 3]
+    if constexpr (MASS_ONLY) return;
+    _Float16(*vrows)[SM::VROW] = sm.v[U % 3];
+    if constexpr (decltype(k_c)::value == kCached) {
+      const typename SM::ZSlot& zs = sm.z[U % 3];
 #pragma unroll
-    for (int mb = 0; mb < 2; mb++)
+      for (int i = 0; i < VGPT; i++) {
+        const int vg = tid + i * kThreads;
+        if (VGROUPS % kThreads != 0 && vg >= VGROUPS) break;
+        const int ch = vg >> 2, g = vg & 3;  // 16-token group g of channel ch
+        const uint4 z0 = *reinterpret_cast<const uint4*>(&zs.zv[8 * g]);
+        const uint4 z1 = *reinterpret_cast<const uint4*>(&zs.zv[8 * g + 4]);
+        const uint4 d0 = *reinterpret_cast<const uint4*>(&zs.dvp[8 * g]);
+        const uint4 d1 = *reinterpret_cast<const uint4*>(&zs.dvp[8 * g + 4]);
+        const uint32_t zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+        const uint32_t dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        uint32_t a[8];
+        if constexpr (BITS == 2) {
+          const uint32_t w = vpre[i].x;
+#pragma unroll
+          for (int j = 0; j < 8; j++) a[j] = ((w >> (2 * j)) & 0x00030003u) | 0x64006400u;
+        } else {
+          // t0 = [w0.b0 w0.b1 w1.b0 w1.b1], t1 = [w0.b2 w0.b3 w1.b2 w1.b3]
+          const uint32_t w0 = vpre[i].x, w1 = vpre[i].y;
+          const uint32_t t0 = (w0 & 0xFFFFu) | (w1 << 16);
+          const uint32_t t1 = (w0 >> 16) | (w1 & 0xFFFF0000u);
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            a[j] = ((t0 >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+            a[4 + j] = ((t1 >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+          }
+        }
+        uint32_t res[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const f16x2 cz = __builtin_bit_cast(f16x2, a[j]) + __builtin_bit_cast(f16x2, zz[j]);  // code - z, exact
+          res[j] = __builtin_bit_cast(uint32_t, cz * __builtin_bit_cast(f16x2, dd[j]));
+        }
+        uint4* dst = reinterpret_cast<uint4*>(&vrows[ch][16 * g]);
+        dst[0] = make_uint4(res[0], res[1], res[2], res[3]);
+        dst[1] = make_uint4(res[4], res[5], res[6], res[7]);
+      }
+    } else {
+      const int t0 = (U - n_ct) * kBN;
+#pragma unroll
+      for (int i = 0; i < VRPT; i++) {
+        const int it = tid + i * kThreads;
+        if (VITEMS % kThreads != 0 && it >= VITEMS) break;
+        const int seg = it % SEGS, pr = it / SEGS;
+        const int pos = 16 * (pr >> 3) + 2 * (pr & 7);  // positions of the pair's tokens: pos, pos+1
+        const int tokA = 16 * (pr >> 3) + (pr & 7);
+        const uint4 zero4 = make_uint4(0, 0, 0, 0);
+        const uint4 va = t0 + tokA < p.n_r ? vpre[2 * i] : zero4;
+        const uint4 vb = t0 + tokA + 8 < p.n_r ? vpre[2 * i + 1] : zero4;
+        const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float a0 = __uint_as_float(wa[e] << 16), a1 = __uint_as_float(wa[e] & 0xFFFF0000u);
+          const float b0 = __uint_as_float(wb[e] << 16), b1 = __uint_as_float(wb[e] & 0xFFFF0000u);
+          *reinterpret_cast<uint32_t*>(&vrows[8 * seg + 2 * e][pos]) = pack_f16x2(a0, b0);
+          *reinterpret_cast<uint32_t*>(&vrows[8 * seg + 2 * e + 1][pos]) = pack_f16x2(a1, b1);
+        }
+      }
+    }
+  };
+
+  // ---------------- stream state ----------------
+  // A block's scores sit in sqh (int32 sums for cached keys, fp32 bits for current
+  // ones) and cb (bias MFMA output) between its QK^T and its softmax; its fp16 P pairs
+  // sit in pb until its PV.
+  float l_s = 0.f, l_r = 0.f;
+  float m_seen = -INFINITY;  // -inf, or a bound of the largest logit of a block that failed
+  f32x16 acc[CBLK];
+  i32x16 sqh[1];
+  f32x16 cb[1];
+  uint32_t pb[2][4];
+#pragma unroll
+  for (int c = 0; c < CBLK; c++) acc[c] = f32x16{};
+
+  // QK^T and bias of block mb of tile U (kind K) into score set SET.
+  auto qk = [&](int U, int mb, auto set_c, auto k_c) KVQ_INLINE {
+    constexpr int SET = decltype(set_c)::value;
+    const typename SM::KSlot& ks = sm.k[U % 3];
+    const typename SM::PSlot& ps = sm.prm[U % 3];
+    const int krow = 32 * mb + mrow_key(col);
+    {
+      const uint4 kb = ps.kb[32 * mb + col][h];
+      const f32x16 zf = {};
+      cb[SET] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kb), qbias, zf, 0, 0, 0);
+    }
+    if constexpr (decltype(k_c)::value == kCached) {
+      // S = 256 S_hi + S_lo in one accumulator: the hi sums, a shift, then the lo sums
+      i32x4 kop[KSTEPS];
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; kk++) kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
+      i32x16 acc_s = {};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; kk++) acc_s = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[kk], qhi[kk], acc_s, 0, 0, 0);
+      acc_s = acc_s << 8;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; kk++) acc_s = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[kk], qlo[kk], acc_s, 0, 0, 0);
+      sqh[SET] = acc_s;
+    } else {
+      f32x16 sc;
+#pragma unroll
+      for (int t = 0; t < D / 16; t++) {
+        const bf16x8 qop = __builtin_bit_cast(bf16x8, t < KSTEPS ? qhi[t] : qlo[t - KSTEPS]);
+        const bf16x8 aop = *reinterpret_cast<const bf16x8*>(&ks.kr[krow][HALF * h + 8 * t]);
+        if (t == 0) {
+          const f32x16 z = {};
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qop, z, 0, 0, 0);
+        } else {
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qop, sc, 0, 0, 0);
+        }
+      }
+      sqh[SET] = __builtin_bit_cast(i32x16, sc);
+    }
+  };
+  // PV of block mb of tile U with the pairs in pb.
+  auto pv = [&](int U, int mb) KVQ_INLINE {
+    if constexpr (!MASS_ONLY) {
+      const _Float16(*vrows)[SM::VROW] = sm.v[U % 3];
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        const f16x8 bop = __builtin_bit_cast(f16x8, make_uint4(pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]));
+#pragma unroll
+        for (int c = 0; c < CBLK; c++) {
+          const f16x8 aop = *reinterpret_cast<const f16x8*>(&vrows[32 * c + col][32 * mb + 16 * ks + 8 * h]);
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, acc[c], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // Logits (log2 units; they carry -m through the bias) of block mb of tile U from SET.
+  auto logits = [&](int U, int mb, auto set_c, auto k_c, float* x) KVQ_INLINE {
+    constexpr int SET = decltype(set_c)::value;
+    if constexpr (decltype(k_c)::value == kCached) {
+      const float* dka = sm.prm[U % 3].dka[wave];
 #pragma unroll
       for (int v4 = 0; v4 < 4; v4++) {
-        const float4 d4 = *reinterpret_cast<const float4*>(&tb.dk[32 * mb + 8 * v4 + 4 * h]);
-        dk[mb][4 * v4] = d4.x; dk[mb][4 * v4 + 1] = d4.y; dk[mb][4 * v4 + 2] = d4.z; dk[mb][4 * v4 + 3] = d4.w;
-      }
-    float pv[2][16];
-    softmax_tile(inner, dk, nvalid < kBN, tb.mask, pv);
+        const float4 d4 = *reinterpret_cast<const float4*>(&dka[32 * mb + 8 * v4 + 4 * h]);
+        const float d[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-    for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-      for (int v = 0; v < 16; v++) l_s += pv[mb][v];
-    if (!MASS_ONLY) {
-      uint32_t pb[4][4];
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; v4++) {
-          const float4 dv4 = *reinterpret_cast<const float4*>(&tb.dv[32 * mb + 8 * v4 + 4 * h]);
-          const int v = 4 * v4;
-          const int ks = 2 * mb + (v4 >> 1), slot = 2 * (v4 & 1);
-          pb[ks][slot] = pack_f16x2(pv[mb][v] * dv4.x, pv[mb][v + 1] * dv4.y);
-          pb[ks][slot + 1] = pack_f16x2(pv[mb][v + 2] * dv4.z, pv[mb][v + 3] * dv4.w);
+        for (int b = 0; b < 4; b++) {
+          const int v = 4 * v4 + b;
+          x[v] = fmaf(d[b], (float)sqh[SET][v], cb[SET][v]);
         }
-      pv_tile(tb, pb);
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; v++) x[v] = fmaf(sl, __int_as_float(sqh[SET][v]), cb[SET][v]);
     }
   };
-
-  if (n_tiles > 0) {
-    load_tile(0);
-    load_zv(0);
-    store_zv(0);
-    if (n_tiles > 1) {
-      load_zv(1);
-      store_zv(1);
+  // fp16 P pairs with p = exp2(x - off) into pb; returns this lane's fp16 sum.
+  auto pairs = [&](const float* x, float off) KVQ_INLINE {
+    float lsum = 0.f;
+    const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+    for (int v2 = 0; v2 < 8; v2++) {
+      const uint32_t pr = pack_f16x2(exp2_(x[2 * v2] - off), exp2_(x[2 * v2 + 1] - off));
+      pb[v2 >> 2][v2 & 3] = pr;
+      lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pr), ones, lsum, false);
     }
-    __syncthreads();
-    store_tile(0, sm.buf[0]);
-    __syncthreads();
-    for (int T = 0; T < n_tiles; T++) {
-      const int cur = T & 1;
-      const bool has_next = T + 1 < n_tiles;
-      if (has_next) load_tile(T + 1);
-      if (T + 2 < n_tiles) load_zv(T + 2);
-      compute_cached(T, sm.buf[cur]);
-      if (has_next) store_tile(T + 1, sm.buf[cur ^ 1]);
-      if (T + 2 < n_tiles) store_zv(cur);  // tile T+2 uses slot (T+2) & 1 == cur
-      __syncthreads();
+    return lsum;
+  };
+  // Softmax numerators of block mb of tile U (scores in SET). The reference m is fixed
+  // for a whole pass over the keys: the maximum of the stream's first block plus a
+  // headroom of 2^8 (FIRST, first pass only), raised only by a restart. A block whose
+  // fp16 row sum passes 2^15 may have left the fp16 range: it records a bound of its
+  // maximum (m + log2 of the sum, at most m + 24) and the pass is repeated.
+  auto softmax = [&](int U, int mb, auto set_c, auto k_c, auto first_c) KVQ_INLINE {
+    float x[16];
+    logits(U, mb, set_c, k_c, x);
+    float lsum = 0.f;
+    bool done = false;
+    if constexpr (decltype(first_c)::value) {
+      if (__builtin_amdgcn_readfirstlane(m_run == -INFINITY ? 1 : 0)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; v++) mx = fmaxf(mx, x[v]);
+        mx = fmaxf(mx, xor32(mx));
+        set_m(mx + kHeadroom);
+        lsum = pairs(x, m_run);
+        done = true;
+      }
     }
-  }
+    if (!done) {
+      lsum = pairs(x, 0.f);
+      const float bound = m_run + fminf(__log2f(lsum), kRaise);
+      m_seen = lsum <= kPmax ? m_seen : fmaxf(m_seen, bound);
+    }
+    if constexpr (decltype(k_c)::value == kCached)
+      l_s += lsum;
+    else
+      l_r += lsum;
+  };
 
-  // ---------------- phase switch: un-rotate the cached PV sum ----------------
-  if (!MASS_ONLY && p.v_had && n_tiles > 0) {
+  auto unrotate = [&]() KVQ_INLINE {
     // acc[c][v] holds channel 32c + (v&3) + 8(v>>2) + 4h of this lane's query.
 #pragma unroll
     for (int bit = 0; bit < 4; bit++) {  // channel bits 0,1 (v bits 0,1) and 3,4 (v bits 2,3)
@@ -555,142 +707,104 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     for (int c = 0; c < CBLK; c++)  // channel bit 2: the partner lane
 #pragma unroll
       for (int v = 0; v < 16; v++) {
-        const float pv = xor32(acc[c][v]);
-        acc[c][v] = h ? (pv - acc[c][v]) : (acc[c][v] + pv);
+        const float pvv = xor32(acc[c][v]);
+        acc[c][v] = h ? (pvv - acc[c][v]) : (acc[c][v] + pvv);
       }
 #pragma unroll
-    for (int cb = 1; cb < CBLK; cb <<= 1)  // channel bits 5, 6: the 32-channel block
+    for (int cbk = 1; cbk < CBLK; cbk <<= 1)  // channel bits 5, 6: the 32-channel block
 #pragma unroll
       for (int c = 0; c < CBLK; c++)
-        if ((c & cb) == 0)
+        if ((c & cbk) == 0)
 #pragma unroll
           for (int v = 0; v < 16; v++) {
-            const float a = acc[c][v], b = acc[c | cb][v];
+            const float a = acc[c][v], b = acc[c | cbk][v];
             acc[c][v] = a + b;
-            acc[c | cb][v] = a - b;
+            acc[c | cbk][v] = a - b;
           }
     const float cn = rsqrtf((float)D);
 #pragma unroll
     for (int c = 0; c < CBLK; c++)
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[c][v] *= cn;
-  }
+  };
 
-  // ---------------- phase 2: current chunk (bf16, no correction) ----------------
-  if (p.n_r > 0) {
-    bf16x8 qb16[D / 16];
-    {
-      const uint16_t* qrow = p.q + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h;
-#pragma unroll
-      for (int t = 0; t < D / 16; t++) {
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (q_ok) w = reinterpret_cast<const uint4*>(qrow)[t];
-        qb16[t] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-    const float sl = p.s * kLog2e;
-    const uint16_t* kr_base = p.k_cur + (size_t)bh * p.n_r * D;
-    const uint16_t* vr_base = p.v_cur + (size_t)bh * p.n_r * D;
-    const int n_rt = (p.n_r + kBN - 1) / kBN;
-    constexpr int SEGS = D / 8;              // 16-byte segments per row
-    constexpr int ITEMS = (kBN / 2) * SEGS;  // (token pair, segment) items per tile
-    static_assert(ITEMS <= kThreads, "one staging item per thread");
-    // thread item: tokens (16g + j, 16g + j + 8) -- adjacent value positions -- and one segment
-    const int seg = tid % SEGS, pr = tid / SEGS;
-    const int tokA = 16 * (pr >> 3) + (pr & 7), tokB = tokA + 8;
-    uint4 rka = make_uint4(0, 0, 0, 0), rkb = rka, rva = rka, rvb = rka;
-    auto load_cur = [&](int T) {
-      if (tid >= ITEMS) return;
-      const int t0 = T * kBN;
-      const bool okA = t0 + tokA < p.n_r, okB = t0 + tokB < p.n_r;
-      rka = rkb = rva = rvb = make_uint4(0, 0, 0, 0);
-      if (okA) {
-        rka = reinterpret_cast<const uint4*>(kr_base + (size_t)(t0 + tokA) * D)[seg];
-        if (!MASS_ONLY) rva = reinterpret_cast<const uint4*>(vr_base + (size_t)(t0 + tokA) * D)[seg];
-      }
-      if (okB) {
-        rkb = reinterpret_cast<const uint4*>(kr_base + (size_t)(t0 + tokB) * D)[seg];
-        if (!MASS_ONLY) rvb = reinterpret_cast<const uint4*>(vr_base + (size_t)(t0 + tokB) * D)[seg];
-      }
-    };
-    auto store_cur = [&](int T, TileBuf<D, BITS>& tb) {
-      if (tid < kBN) {
-        const int nvalid = min(kBN, p.n_r - T * kBN);
-        tb.mask[32 * (tid >> 5) + key_mrow(tid & 31)] = tid < nvalid ? 0.f : -INFINITY;
-      }
-      if (tid >= ITEMS) return;
-      *reinterpret_cast<uint4*>(&tb.kr[tokA][8 * seg]) = rka;
-      *reinterpret_cast<uint4*>(&tb.kr[tokB][8 * seg]) = rkb;
-      if (!MASS_ONLY) {
-        const uint32_t wa[4] = {rva.x, rva.y, rva.z, rva.w}, wb[4] = {rvb.x, rvb.y, rvb.z, rvb.w};
-        const int pos = 16 * (pr >> 3) + 2 * (pr & 7);  // positions of tokA, tokB: pos, pos + 1
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const float a0 = __uint_as_float(wa[e] << 16), a1 = __uint_as_float(wa[e] & 0xFFFF0000u);
-          const float b0 = __uint_as_float(wb[e] << 16), b1 = __uint_as_float(wb[e] & 0xFFFF0000u);
-          *reinterpret_cast<uint32_t*>(&tb.v[8 * seg + 2 * e][pos]) = pack_f16x2(a0, b0);
-          *reinterpret_cast<uint32_t*>(&tb.v[8 * seg + 2 * e + 1][pos]) = pack_f16x2(a1, b1);
-        }
-      }
-    };
-    auto compute_cur = [&](int T, const TileBuf<D, BITS>& tb) {
-      const int nvalid = min(kBN, p.n_r - T * kBN);
-      f32x16 sc[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++) {
-        const int key = 32 * mb + mrow_key(col);
-#pragma unroll
-        for (int t = 0; t < D / 16; t++) {
-          const bf16x8 aop = *reinterpret_cast<const bf16x8*>(&tb.kr[key][HALF * h + 8 * t]);
-          if (t == 0) {
-            const f32x16 z = {};
-            sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb16[t], z, 0, 0, 0);
-          } else {
-            sc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qb16[t], sc[mb], 0, 0, 0);
-          }
-        }
-      }
-      float slv[2][16];
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-        for (int v = 0; v < 16; v++) slv[mb][v] = sl;
-      float pv[2][16];
-      softmax_tile(sc, slv, nvalid < kBN, tb.mask, pv);
-#pragma unroll
-      for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-        for (int v = 0; v < 16; v++) l_r += pv[mb][v];
-      if (!MASS_ONLY) {
-        uint32_t pb[4][4];
-#pragma unroll
-        for (int mb = 0; mb < 2; mb++)
-#pragma unroll
-          for (int v4 = 0; v4 < 4; v4++) {
-            const int v = 4 * v4;
-            const int ks = 2 * mb + (v4 >> 1), slot = 2 * (v4 & 1);
-            pb[ks][slot] = pack_f16x2(pv[mb][v], pv[mb][v + 1]);
-            pb[ks][slot + 1] = pack_f16x2(pv[mb][v + 2], pv[mb][v + 3]);
-          }
-        pv_tile(tb, pb);
-      }
-    };
-    load_cur(0);
-    store_cur(0, sm.buf[0]);
+  // Step T of a run of n_t tiles of one kind (tile index U = U0 + T): QK^T, softmax and
+  // PV of the tile's two 32-key blocks, while the keys of tile U+2 and the values of
+  // tile U+1 are staged. FIRST: block (U,0) may be the stream's first.
+  auto step = [&](int U0, int n_t, int T, auto k_c, auto first_c) KVQ_INLINE {
+    const Kind<0> set0;
+    const std::false_type no;
+    const int U = U0 + T;
+    const bool stage_k = T + 2 < n_t, stage_v = T + 1 < n_t;
+    if (stage_k) load_k(U + 2, k_c);
+    if (stage_v) load_v(U + 1, k_c);
+    qk(U, 0, set0, k_c);
+    softmax(U, 0, set0, k_c, first_c);
+    pv(U, 0);
+    qk(U, 1, set0, k_c);
+    softmax(U, 1, set0, k_c, no);
+    pv(U, 1);
+    if (stage_k) store_k(U + 2, k_c);
+    if (stage_v) store_v(U + 1, k_c);
     __syncthreads();
-    for (int T = 0; T < n_rt; T++) {
-      const bool has_next = T + 1 < n_rt;
-      if (has_next) load_cur(T + 1);
-      compute_cur(T, sm.buf[T & 1]);
-      if (has_next) store_cur(T + 1, sm.buf[(T + 1) & 1]);
-      __syncthreads();
+  };
+  // All tiles of one kind: stage the first two tiles' keys and the first values, then
+  // run the steps.
+  auto run = [&](int U0, int n_t, auto k_c) KVQ_INLINE {
+    const std::false_type no;
+    load_k(U0, k_c);
+    store_k(U0, k_c);
+    if (n_t > 1) {
+      load_k(U0 + 1, k_c);
+      store_k(U0 + 1, k_c);
     }
+    __syncthreads();
+    load_v(U0, k_c);
+    store_v(U0, k_c);
+    __syncthreads();
+    step(U0, n_t, 0, k_c, std::true_type());
+    for (int T = 1; T < n_t; T++) step(U0, n_t, T, k_c, no);
+  };
+
+  // ---------------- passes over the keys ----------------
+  // A pass repeats only if some block's numerators may have left the fp16 range; it
+  // then starts from the recorded bounds, which raise m by log2 of the offending row
+  // sum (at least 15, at most 24 per pass).
+  for (int pass = 0; pass < kMaxPasses; pass++) {
+    if (n_ct > 0) {
+      run(0, n_ct, Kind<kCached>());
+      if constexpr (!MASS_ONLY) {
+        if (p.v_had) unrotate();
+      }
+    }
+    if (n_rt > 0) {
+      load_query_bf16();
+      run(n_ct, n_rt, Kind<kCurrent>());
+    }
+    if (tid == 0) sm.fail = 0;
+    __syncthreads();
+    if (__ballot(m_seen != -INFINITY) != 0 && lane == 0) sm.fail = 1;
+    __syncthreads();
+    if (sm.fail == 0 || pass + 1 == kMaxPasses) break;
+    // restart from the recorded bounds; the int8 query operands (replaced by the bf16
+    // query for the current chunk) and the bias operand are rebuilt with the new m
+    {
+      _Float16 mh, ml;
+      split16(-fmaxf(m_run, fmaxf(m_seen, xor32(m_seen))), mh, ml);
+      m_run = -((float)mh + (float)ml);
+    }
+    m_seen = -INFINITY;
+    l_s = 0.f;
+    l_r = 0.f;
+#pragma unroll
+    for (int c = 0; c < CBLK; c++) acc[c] = f32x16{};
+    build_query();
   }
 
   // ---------------- epilogue ----------------
-  l_s += xor32(l_s);
-  l_r += xor32(l_r);
-  const float tot = l_s + l_r;
+  const float ls = l_s + xor32(l_s);
+  const float lr = l_r + xor32(l_r);
+  const float tot = ls + lr;
   if (!q_ok) return;
   const float inv = 1.f / tot;
   if (!MASS_ONLY) {
@@ -705,8 +819,8 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       }
   }
   if (h == 0 && p.mass_s) {
-    p.mass_s[(size_t)bh * p.n_q + qi] = l_s * inv;
-    p.mass_r[(size_t)bh * p.n_q + qi] = l_r * inv;
+    p.mass_s[(size_t)bh * p.n_q + qi] = ls * inv;
+    p.mass_r[(size_t)bh * p.n_q + qi] = lr * inv;
   }
 }
 

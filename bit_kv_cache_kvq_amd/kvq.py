@@ -13,7 +13,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libkvq.so")
+# KVQ_LIBRARY overrides the library file (development builds of kernel variants)
+library_path = os.environ.get("KVQ_LIBRARY") or os.path.join(_HERE, "libkvq.so")
 
 KVQ_PER_TOKEN, KVQ_PER_CHANNEL = 0, 1
 KVQ_ROLE_KEY, KVQ_ROLE_VALUE = 0, 1

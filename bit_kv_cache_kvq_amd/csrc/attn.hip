@@ -24,11 +24,16 @@
 //    (hi/lo fp16 pairs), 1 and the mask, and whose query operand holds -A sum(q_f),
 //    -G, -m and a large negative constant. In log2 units the logit is
 //    x = (Delta_j A) S + c with A = s sigma log2 e and G = s^2 |q'|^2 / 24 log2 e, so a
-//    score costs a shift-add, a convert, one fma and one exp2.
-//  * The reference max m is fixed for a whole pass over the keys: the first block's
-//    maximum plus a headroom of 2^8. p = exp2(x) then needs no rescaling of the
-//    accumulator; a block whose fp16 row sum passes 2^15 records a bound of its maximum
-//    and the workgroup repeats the pass with the raised m (rare; bounded).
+//    score costs a convert, one fma and one exp2 (the int8 MFMAs accumulate the hi sums,
+//    shift them by 8 and add the lo sums in the same int32 accumulator).
+//  * Keys quantized per channel over token groups (Delta_gc, z_gc): at each group's
+//    first tile the wave rescales its rotated query by the group's steps, re-quantizes
+//    it (scale a_ch) and folds the group's zero-point and correction terms into a
+//    per-query constant carried by the bias MFMA; the logit is x = a_ch S + c.
+//  * The reference max m starts at the first block's maximum plus a headroom of 2^8 and
+//    stays fixed while every p = exp2(x) fits fp16 (checked by the fp16 row sum of each
+//    block); only a block that passes 2^15 raises m and rescales the accumulator, in a
+//    rare wave-uniform branch.
 //  * PV on fp16 MFMA: P = fp16(p) straight from the score registers (a fixed key
 //    permutation inside each 32-key block makes the score layout the B operand); the
 //    value tile in LDS holds fp16((code - z) Delta^V), exact in the subtraction. The
@@ -64,8 +69,6 @@ constexpr int kBN = 64;                 // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPmax = 32768.f;     // largest fp16 row sum of a block accepted in a pass
 constexpr float kHeadroom = 8.f;     // first reference max: the first block's max + 8 (log2 units)
-constexpr float kRaise = 24.f;       // largest raise of the reference max per restart (log2 units)
-constexpr int kMaxPasses = 8;        // passes over the keys (restarts are rare; see the softmax)
 constexpr float kMaskLogit = 65504.f;  // subtracted from padded keys' logits (log2 units)
 constexpr float kD2Scale = 64.f;     // Delta^2 is carried as Delta^2 / 64 (fp16 range)
 
@@ -86,6 +89,7 @@ struct Params {
   float s;
   int correction;
   int k_had, v_had;
+  int k_group;  // tokens per key channel group (per-channel keys), else 0
   float* o;
   float* mass_s;
   float* mass_r;
@@ -161,7 +165,6 @@ struct Smem {
   alignas(16) PSlot prm[3];
   alignas(16) ZSlot z[3];
   alignas(16) float a_stream[kNS];
-  int fail;
 };
 
 #define KVQ_INLINE __attribute__((always_inline))
@@ -170,7 +173,7 @@ enum : int { kNone = 0, kCached = 1, kCurrent = 2 };
 template <int K>
 using Kind = std::integral_constant<int, K>;
 
-template <int D, int BITS, bool MASS_ONLY>
+template <int D, int BITS, bool MASS_ONLY, bool PERCH>
 __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   using SM = Smem<D>;
   constexpr int HALF = D / 2;
@@ -211,8 +214,8 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   f16x8 qbias;                     // query operand of the bias MFMA
   float m_run = -INFINITY;         // reference max (log2 units); -inf until the first block
   float a_st = 0.f;                // A of this wave's stream
-  auto build_query = [&]() KVQ_INLINE {
-    float qv[HALF];
+  // Rotated query q' = H q / sqrt(d) (or q) of this lane's half: channels HALF h + i.
+  auto rotated_query = [&](float* qv) KVQ_INLINE {
     const uint16_t* qrow = p.q + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h;
 #pragma unroll
     for (int u = 0; u < HALF / 8; u++) {
@@ -242,6 +245,18 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         qv[i] = (h ? (pv - qv[i]) : (qv[i] + pv)) * c;
       }
     }
+  };
+  // -m, plus the key group's constant c_grp (per-channel keys), into query slots 8, 9.
+  float c_grp = 0.f;
+  auto write_mslot = [&]() KVQ_INLINE {
+    _Float16 mh = (_Float16)0.f, ml = (_Float16)0.f;
+    split16(c_grp - (m_run == -INFINITY ? 0.f : m_run), mh, ml);
+    qbias[0] = h ? mh : qbias[0];
+    qbias[1] = h ? ml : qbias[1];
+  };
+  auto build_query = [&]() KVQ_INLINE {
+    float qv[HALF];
+    rotated_query(qv);
     float ss = 0.f, mxa = 0.f;
 #pragma unroll
     for (int i = 0; i < HALF; i++) {
@@ -290,15 +305,11 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       qbias[6] = (_Float16)0.f;
       qbias[7] = (_Float16)0.f;
     } else {
-      // -m (hi, lo); 0 while m is unset
-      _Float16 mh = (_Float16)0.f, ml = (_Float16)0.f;
-      if (m_run != -INFINITY) split16(-m_run, mh, ml);
-      qbias[0] = mh;
-      qbias[1] = ml;
       qbias[2] = (_Float16)(-kMaskLogit);
 #pragma unroll
       for (int e = 3; e < 8; e++) qbias[e] = (_Float16)0.f;
     }
+    write_mslot();  // -m (hi, lo); 0 while m is unset
     if (lane == 0) sm.a_stream[wave] = A;
     __syncthreads();
     a_st = sm.a_stream[wave];
@@ -317,14 +328,17 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         qlo[t - KSTEPS] = __builtin_bit_cast(i32x4, w);
     }
   };
-  // Sets the reference max to mx, rounded to what the bias operand carries (-m as an
-  // fp16 hi + lo pair in query slots 8, 9).
+  // Sets the reference max to mx; with per-token keys m is rounded to what the bias
+  // operand carries (-m as an fp16 hi + lo pair), so that every block sees the same m.
   auto set_m = [&](float mx) KVQ_INLINE {
-    _Float16 mh, ml;
-    split16(-mx, mh, ml);
-    m_run = -((float)mh + (float)ml);
-    qbias[0] = h ? mh : qbias[0];
-    qbias[1] = h ? ml : qbias[1];
+    if constexpr (PERCH) {
+      m_run = mx;
+    } else {
+      _Float16 mh, ml;
+      split16(-mx, mh, ml);
+      m_run = -((float)mh + (float)ml);
+    }
+    write_mslot();
   };
   build_query();
 
@@ -343,6 +357,75 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   const uint16_t* vr_base = p.v_cur + (size_t)bh * p.n_r * D;
   auto n_valid = [&](int U) KVQ_INLINE {
     return U < n_ct ? min(kBN, p.chunk_len - (U % tiles_per_chunk) * kBN) : min(kBN, p.n_r - (U - n_ct) * kBN);
+  };
+
+  // Per-channel keys: a key of channel group g (of its chunk) dequantizes as
+  // Delta_gc (code_c - z_gc), so its logit is s q~.code - s q~.z_g - b - m with
+  // q~_c = q'_c Delta_gc and b = s^2 |q~|^2 / 24 (the per-channel Taylor correction).
+  // At each group's first tile the wave rebuilds the int8 operands from q~ (own scale
+  // a_ch) and folds the group constant c_grp = -a_ch sum(q~_f z_g) - G into the bias.
+  const int k_tpg = PERCH ? p.k_group / kBN : 1;                       // tiles per key group
+  const int k_gpc = PERCH ? (p.chunk_len + p.k_group - 1) / p.k_group : 1;  // groups per chunk
+  float a_ch = 0.f;
+  auto refresh_group = [&](int U) KVQ_INLINE {
+    const int ci = U / tiles_per_chunk, t = U % tiles_per_chunk;
+    const size_t gi = (size_t)ci * k_gpc + t / k_tpg;
+    const size_t prow = ((size_t)bh * p.n_chunks * k_gpc + gi) * D + HALF * h;
+    const uint4* drow = reinterpret_cast<const uint4*>(p.k_scale + prow);
+    const uint4* zrow = reinterpret_cast<const uint4*>(p.k_zero + prow);
+    float qv[HALF];
+    rotated_query(qv);
+    float ss = 0.f, mxa = 0.f;
+#pragma unroll
+    for (int u = 0; u < HALF / 8; u++) {
+      const uint4 w = drow[u];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float dl = half_bits_to_f32(e & 1 ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu);
+        const float qt = qv[8 * u + e] * dl;
+        qv[8 * u + e] = qt;
+        ss += qt * qt;
+        mxa = fmaxf(mxa, fabsf(qt));
+      }
+    }
+    ss += xor32(ss);
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));  // stream-wide max
+    const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
+    a_ch = mxa > 0.f ? sl * (mxa / kQFix) : 0.f;
+    float zs = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; kk++) {
+      float zt[16];
+#pragma unroll
+      for (int u2 = 0; u2 < 2; u2++) {
+        const uint4 w = zrow[2 * kk + u2];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 8; e++) zt[8 * u2 + e] = half_bits_to_f32(e & 1 ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        uint32_t whi = 0, wlo = 0;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const int c = kperm<BITS>(j, b);
+          const int qf = (int)__builtin_rintf(qv[16 * kk + c] * inv);
+          const int hi = (qf + 128) >> 8;
+          const int lo = qf - (hi << 8);
+          zs = fmaf((float)qf, zt[c], zs);
+          whi |= (uint32_t)(hi & 0xFF) << (8 * b);
+          wlo |= (uint32_t)(lo & 0xFF) << (8 * b);
+        }
+        qhi[kk][j] = (int)whi;
+        qlo[kk][j] = (int)wlo;
+      }
+    }
+    zs += xor32(zs);
+    const float G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
+    c_grp = -a_ch * zs - G;
+    write_mslot();
   };
 
   // ---------------- staging (all threads) ----------------
@@ -370,8 +453,10 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
           kpre[i].x = src[0];
         }
       }
-      pk_dk = ks_base[tok0 + (tid & (kBN - 1))];
-      pk_zk = kz_base[tok0 + (tid & (kBN - 1))];
+      if constexpr (!PERCH) {
+        pk_dk = ks_base[tok0 + (tid & (kBN - 1))];
+        pk_zk = kz_base[tok0 + (tid & (kBN - 1))];
+      }
       if constexpr (!MASS_ONLY) {
         const int g = (tid >> 3) & 3, j = tid & 7;
         pz0 = vz_base[tok0 + 16 * g + j];
@@ -410,13 +495,17 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         *reinterpret_cast<uint4*>(&ks.c[tok][16 * ui]) = lo;
       }
       // Delta_j A of each wave's stream; 0 for padding keys (their logit is set by the mask)
-      {
+      if constexpr (!PERCH) {
         const int key = tid & (kBN - 1);
         const int r = 32 * (key >> 5) + key_mrow(key & 31);
         const float dk = key < nv ? half_bits_to_f32(pk_dk) : 0.f;
         ps.dka[wave][r] = dk * a_st;
       }
-      if (wave == 0) {
+      if (PERCH && wave == 0) {
+        // per-channel keys: the group terms ride on the query side (slots 8, 9)
+        const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
+        ps.kb[r][0] = make_uint4(0, 0, 0, 0);
+      } else if (wave == 0) {
         // bias key operand, slots 0..7: dz_hi, dz_hi, dz_lo, d2_hi, d2_hi, d2_lo, 0, 0
         const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
         uint4 row = make_uint4(0, 0, 0, 0);
@@ -563,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   // ones) and cb (bias MFMA output) between its QK^T and its softmax; its fp16 P pairs
   // sit in pb until its PV.
   float l_s = 0.f, l_r = 0.f;
-  float m_seen = -INFINITY;  // -inf, or a bound of the largest logit of a block that failed
+
   f32x16 acc[CBLK];
   i32x16 sqh[1];
   f32x16 cb[1];
@@ -628,7 +717,10 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   // Logits (log2 units; they carry -m through the bias) of block mb of tile U from SET.
   auto logits = [&](int U, int mb, auto set_c, auto k_c, float* x) KVQ_INLINE {
     constexpr int SET = decltype(set_c)::value;
-    if constexpr (decltype(k_c)::value == kCached) {
+    if constexpr (decltype(k_c)::value == kCached && PERCH) {
+#pragma unroll
+      for (int v = 0; v < 16; v++) x[v] = fmaf(a_ch, (float)sqh[SET][v], cb[SET][v]);
+    } else if constexpr (decltype(k_c)::value == kCached) {
       const float* dka = sm.prm[U % 3].dka[wave];
 #pragma unroll
       for (int v4 = 0; v4 < 4; v4++) {
@@ -657,11 +749,11 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     }
     return lsum;
   };
-  // Softmax numerators of block mb of tile U (scores in SET). The reference m is fixed
-  // for a whole pass over the keys: the maximum of the stream's first block plus a
-  // headroom of 2^8 (FIRST, first pass only), raised only by a restart. A block whose
-  // fp16 row sum passes 2^15 may have left the fp16 range: it records a bound of its
-  // maximum (m + log2 of the sum, at most m + 24) and the pass is repeated.
+  // Softmax numerators of block mb of tile U (scores in SET). The reference m starts at
+  // the maximum of the stream's first block plus a headroom of 2^8 (FIRST) and is raised
+  // only when a block's fp16 row sum passes 2^15 (some p may have left the fp16 range):
+  // then m becomes that block's maximum, the sums and the accumulator are rescaled and
+  // the block's p recomputed (a rare, wave-uniform branch).
   auto softmax = [&](int U, int mb, auto set_c, auto k_c, auto first_c) KVQ_INLINE {
     float x[16];
     logits(U, mb, set_c, k_c, x);
@@ -680,8 +772,28 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     }
     if (!done) {
       lsum = pairs(x, 0.f);
-      const float bound = m_run + fminf(__log2f(lsum), kRaise);
-      m_seen = lsum <= kPmax ? m_seen : fmaxf(m_seen, bound);
+      const bool raise = !(lsum <= kPmax);
+      if (__ballot(raise) != 0) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; v++) mx = fmaxf(mx, x[v]);
+        mx = fmaxf(mx, xor32(mx));
+        // either half of the query (the shuffle runs on every lane, outside any ||)
+        const float partner_raise = xor32(raise ? 1.f : 0.f);
+        const bool up = raise || partner_raise != 0.f;
+        const float m_old = m_run;
+        set_m(up ? m_old + mx : m_old);
+        const float sc = exp2_(m_old - m_run);
+        l_s *= sc;
+        l_r *= sc;
+        if constexpr (!MASS_ONLY) {
+#pragma unroll
+          for (int c = 0; c < CBLK; c++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[c][v] *= sc;
+        }
+        lsum = pairs(x, m_run - m_old);
+      }
     }
     if constexpr (decltype(k_c)::value == kCached)
       l_s += lsum;
@@ -738,6 +850,9 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     const bool stage_k = T + 2 < n_t, stage_v = T + 1 < n_t;
     if (stage_k) load_k(U + 2, k_c);
     if (stage_v) load_v(U + 1, k_c);
+    if constexpr (PERCH && decltype(k_c)::value == kCached) {
+      if ((U % tiles_per_chunk) % k_tpg == 0) refresh_group(U);
+    }
     qk(U, 0, set0, k_c);
     softmax(U, 0, set0, k_c, first_c);
     pv(U, 0);
@@ -766,39 +881,20 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     for (int T = 1; T < n_t; T++) step(U0, n_t, T, k_c, no);
   };
 
-  // ---------------- passes over the keys ----------------
-  // A pass repeats only if some block's numerators may have left the fp16 range; it
-  // then starts from the recorded bounds, which raise m by log2 of the offending row
-  // sum (at least 15, at most 24 per pass).
-  for (int pass = 0; pass < kMaxPasses; pass++) {
-    if (n_ct > 0) {
-      run(0, n_ct, Kind<kCached>());
-      if constexpr (!MASS_ONLY) {
-        if (p.v_had) unrotate();
-      }
+  // ---------------- the cached window, then the current chunk ----------------
+  if (n_ct > 0) {
+    run(0, n_ct, Kind<kCached>());
+    if constexpr (!MASS_ONLY) {
+      if (p.v_had) unrotate();
     }
-    if (n_rt > 0) {
-      load_query_bf16();
-      run(n_ct, n_rt, Kind<kCurrent>());
+  }
+  if (n_rt > 0) {
+    load_query_bf16();
+    if constexpr (PERCH) {
+      c_grp = 0.f;
+      write_mslot();
     }
-    if (tid == 0) sm.fail = 0;
-    __syncthreads();
-    if (__ballot(m_seen != -INFINITY) != 0 && lane == 0) sm.fail = 1;
-    __syncthreads();
-    if (sm.fail == 0 || pass + 1 == kMaxPasses) break;
-    // restart from the recorded bounds; the int8 query operands (replaced by the bf16
-    // query for the current chunk) and the bias operand are rebuilt with the new m
-    {
-      _Float16 mh, ml;
-      split16(-fmaxf(m_run, fmaxf(m_seen, xor32(m_seen))), mh, ml);
-      m_run = -((float)mh + (float)ml);
-    }
-    m_seen = -INFINITY;
-    l_s = 0.f;
-    l_r = 0.f;
-#pragma unroll
-    for (int c = 0; c < CBLK; c++) acc[c] = f32x16{};
-    build_query();
+    run(n_ct, n_rt, Kind<kCurrent>());
   }
 
   // ---------------- epilogue ----------------
@@ -832,7 +928,8 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   if (vf.bits != kf.bits) return KVQ_ERR_UNSUPPORTED;
   if (kf.role != KVQ_ROLE_KEY || vf.role != KVQ_ROLE_VALUE) return KVQ_ERR_UNSUPPORTED;
   if (vf.granularity != KVQ_PER_TOKEN) return KVQ_ERR_UNSUPPORTED;
-  if (kf.granularity != KVQ_PER_TOKEN) return KVQ_ERR_UNSUPPORTED;  // per-channel keys: see jb_attn_fwd
+  if (kf.granularity != KVQ_PER_TOKEN && kf.granularity != KVQ_PER_CHANNEL) return KVQ_ERR_UNSUPPORTED;
+  if (kf.granularity == KVQ_PER_CHANNEL && kf.group != 64 && kf.group != 128) return KVQ_ERR_UNSUPPORTED;
   if ((kf.hadamard | vf.hadamard) & ~1) return KVQ_ERR_UNSUPPORTED;
   if (a->correction != JB_CORR_NONE && a->correction != JB_CORR_TAYLOR) return KVQ_ERR_UNSUPPORTED;
   if (a->d != 64 && a->d != 128) return KVQ_ERR_SHAPE;
@@ -863,7 +960,7 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   return KVQ_OK;
 }
 
-template <int D, int BITS, bool MASS_ONLY>
+template <int D, int BITS, bool MASS_ONLY, bool PERCH>
 int launch_attn(const jb_attn_args* a, hipStream_t st) {
   Params p;
   p.B = a->B;
@@ -887,11 +984,12 @@ int launch_attn(const jb_attn_args* a, hipStream_t st) {
   p.correction = a->correction;
   p.k_had = a->k_fmt.hadamard;
   p.v_had = a->v_fmt.hadamard;
+  p.k_group = PERCH ? a->k_fmt.group : 0;
   p.o = MASS_ONLY ? nullptr : a->o;
   p.mass_s = a->mass_s;
   p.mass_r = a->mass_r;
   const unsigned grid = (unsigned)(p.n_qblk * a->B * a->H);
-  jb_attn_kernel<D, BITS, MASS_ONLY><<<grid, kThreads, 0, st>>>(p);
+  jb_attn_kernel<D, BITS, MASS_ONLY, PERCH><<<grid, kThreads, 0, st>>>(p);
   return launch_status();
 }
 
@@ -900,9 +998,15 @@ int dispatch(const jb_attn_args* a, void* stream) {
   const int st = validate_attn(a, MASS_ONLY);
   if (st) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (a->d == 128)
-    return a->k_fmt.bits == 2 ? launch_attn<128, 2, MASS_ONLY>(a, s) : launch_attn<128, 4, MASS_ONLY>(a, s);
-  return a->k_fmt.bits == 2 ? launch_attn<64, 2, MASS_ONLY>(a, s) : launch_attn<64, 4, MASS_ONLY>(a, s);
+  const bool perch = a->k_fmt.granularity == KVQ_PER_CHANNEL;
+  if (a->d == 128) {
+    if (a->k_fmt.bits == 2)
+      return perch ? launch_attn<128, 2, MASS_ONLY, true>(a, s) : launch_attn<128, 2, MASS_ONLY, false>(a, s);
+    return perch ? launch_attn<128, 4, MASS_ONLY, true>(a, s) : launch_attn<128, 4, MASS_ONLY, false>(a, s);
+  }
+  if (a->k_fmt.bits == 2)
+    return perch ? launch_attn<64, 2, MASS_ONLY, true>(a, s) : launch_attn<64, 2, MASS_ONLY, false>(a, s);
+  return perch ? launch_attn<64, 4, MASS_ONLY, true>(a, s) : launch_attn<64, 4, MASS_ONLY, false>(a, s);
 }
 
 }  // namespace

@@ -75,7 +75,7 @@ def test_tiny_all_rows(correction):
 
 
 # (name, rows per sampled head)
-FULL = [("c24", 96), ("c40", 64), ("long", 32)]
+FULL = [("c24", 96), ("c40", 64), ("c40_perch", 64), ("long", 32)]
 
 
 @pytest.mark.parametrize("name,nrows", FULL)
@@ -125,6 +125,54 @@ def test_edges_all_rows(shape, bits):
     Or, PSr, PRr = run_oracle(x, w)
     assert_attention_close(O, Or, f"edge {shape}")
     assert_mass_close(PS, PR, PSr, PRr, f"edge {shape}")
+
+
+# per-channel keys (one step pair per channel over a token group): groups of 64 and 128,
+# ragged last groups and ragged tiles, both bit widths, with and without correction
+PERCH = [
+    dict(B=1, H=2, d=128, n_q=200, chunk_len=300, n_chunks=3, group=128),  # short last group (44)
+    dict(B=1, H=2, d=64, n_q=130, chunk_len=128, n_chunks=2, group=64),
+    dict(B=1, H=1, d=128, n_q=64, chunk_len=70, n_chunks=4, group=64),     # 6-token last group
+    dict(B=2, H=1, d=64, n_q=33, chunk_len=256, n_chunks=1, group=128),
+]
+
+
+@pytest.mark.parametrize("shape", PERCH, ids=lambda s: "x".join(str(v) for v in s.values()))
+@pytest.mark.parametrize("bits,correction", [(2, 1), (4, 1), (2, 0)])
+def test_per_channel_keys_all_rows(shape, bits, correction):
+    w = synth.Workload("perch", **shape, bits=bits, k_dist="t3", k_granularity="channel", seed=11)
+    print(f"attn per-channel {shape} bits={bits} correction={correction}", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w, correction=correction)
+    Or, PSr, PRr = run_oracle(x, w, correction="taylor" if correction else "none")
+    assert_attention_close(O, Or, f"perch {shape} b{bits} c{correction}")
+    assert_mass_close(PS, PR, PSr, PRr, f"perch {shape} b{bits} c{correction}")
+
+
+def _bf16_bits(a):
+    u = np.asarray(a, np.float32).view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("gain", [3.0, 6.0, 12.0])
+def test_late_dominant_key(gain):
+    """A key near the window's end scores tens of nats above the first keys, past what
+    fp16 numerators relative to the first keys can hold: the kernel has to raise its
+    reference max and repeat the pass (once, and several times for the largest gain)."""
+    w = synth.Workload("late", B=1, H=1, d=64, n_q=64, chunk_len=128, n_chunks=3)
+    x = synth.draw_all(w)
+    q = np.ones((1, 1, w.n_q, w.d), np.float32)
+    q[..., 1::2] = -1.0
+    x["q"] = _bf16_bits(q)
+    k = x["k_cache"].copy()
+    big = _bf16_bits(q[0, 0, 0] * gain)
+    k[0, 0, 2 * w.chunk_len + 100] = big      # third chunk
+    x["k_cache"] = k
+    print(f"attn late dominant key, gain {gain}", flush=True)
+    O, PS, PR = run_gpu(x, w)
+    Or, PSr, PRr = run_oracle(x, w)
+    assert_attention_close(O, Or, f"late key {gain}")
+    assert_mass_close(PS, PR, PSr, PRr, f"late key {gain}")
 
 
 def test_no_current_chunk():

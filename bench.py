@@ -86,7 +86,7 @@ def main():
     ap.add_argument("--workload", default="c40")
     ap.add_argument("--bits", type=int, default=None)
     ap.add_argument("--correction", type=int, default=1)
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads in the oracle timing sample (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle timing sample (0: skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="only run a device copy of this many MiB (HBM counter calibration) and exit")
     args = ap.parse_args()

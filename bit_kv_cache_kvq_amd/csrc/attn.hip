@@ -30,7 +30,8 @@
 //    first tile the wave rescales its rotated query by the group's steps, re-quantizes
 //    it (scale a_ch) and folds the group's zero-point and correction terms into a
 //    per-query constant carried by the bias MFMA; the logit is x = a_ch S + c.
-//  * The reference max m starts at the first block's maximum plus a headroom of 2^8 and
+//  * The reference max m starts at the first block's maximum plus a headroom of 2^2 (a
+//    larger headroom pushes keys a few binades below the max into fp16 subnormals) and
 //    stays fixed while every p = exp2(x) fits fp16 (checked by the fp16 row sum of each
 //    block); only a block that passes 2^15 raises m and rescales the accumulator, in a
 //    rare wave-uniform branch.
@@ -68,7 +69,7 @@ constexpr int kBM = 32 * kNS;           // queries per workgroup
 constexpr int kBN = 64;                 // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPmax = 32768.f;     // largest fp16 row sum of a block accepted in a pass
-constexpr float kHeadroom = 8.f;     // first reference max: the first block's max + 8 (log2 units)
+constexpr float kHeadroom = 2.f;     // first reference max: the first block's max + 2 (log2 units)
 constexpr float kMaskLogit = 65504.f;  // subtracted from padded keys' logits (log2 units)
 constexpr float kD2Scale = 64.f;     // Delta^2 is carried as Delta^2 / 64 (fp16 range)
 
@@ -750,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     return lsum;
   };
   // Softmax numerators of block mb of tile U (scores in SET). The reference m starts at
-  // the maximum of the stream's first block plus a headroom of 2^8 (FIRST) and is raised
+  // the maximum of the stream's first block plus a headroom of 2^2 (FIRST) and is raised
   // only when a block's fp16 row sum passes 2^15 (some p may have left the fp16 range):
   // then m becomes that block's maximum, the sums and the accumulator are rescaled and
   // the block's p recomputed (a rare, wave-uniform branch).

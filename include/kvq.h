@@ -140,6 +140,12 @@ typedef struct {
 } jb_attn_args;
 
 /* Corrected attention forward: writes o and, if given, mass_s/mass_r.
+ * Numerics: cached-key scores use the rotated query as a 16-bit fixed-point integer
+ * (one scale per 32 queries) against the exact integer codes; softmax numerators are
+ * fp16 (relative to a per-query reference max that is raised whenever a numerator could
+ * leave the fp16 range), values fp16((code - z) Delta); sums and outputs fp32.
+ * Preconditions on the data (not checked): key steps Delta < 2048 and |Delta z| < 65504
+ * (per token), scaled logits |s q.k| and the correction below 2^15 nats.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED (mixed bits, value per-channel,
  * wrong roles, group not 64/128), KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
 int jb_attn_fwd(const jb_attn_args* a, void* stream);

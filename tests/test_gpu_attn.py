@@ -93,6 +93,23 @@ def test_workload_sampled_rows(name, nrows):
     assert np.all(np.isfinite(O))
 
 
+# every row of a few full-size heads (head (0, 12) of c40 holds rows whose attention mass
+# sits a few binades below the first keys' maximum)
+FULL_HEADS = [("c40", (0, 12)), ("c40", (0, 31)), ("c24", (0, 5)), ("c40_perch", (0, 7))]
+
+
+@pytest.mark.parametrize("name,head", FULL_HEADS, ids=lambda v: str(v))
+def test_workload_all_rows_of_one_head(name, head):
+    w = synth.WORKLOADS[name]
+    print(f"attn {name}: every row of head {head}", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w, masses=True)
+    Or, PSr, PRr = run_oracle(x, w, heads=[head])
+    b, h = head
+    assert_attention_close(O[b, h][None, None], Or, f"{name} head {head}")
+    assert_mass_close(PS[b, h][None, None], PR[b, h][None, None], PSr, PRr, f"{name} head {head}")
+
+
 def test_c40_int4_sampled_rows():
     w = synth.WORKLOADS["c40"].replace(bits=4)
     print("attn c40 int4", flush=True)

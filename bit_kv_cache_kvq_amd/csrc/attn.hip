@@ -130,6 +130,13 @@ __device__ inline void split16(float x, _Float16& hi, _Float16& lo) {
 }
 
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32); }
+
+// Raw buffer descriptor over [base, base + bytes): loads take a per-lane 32-bit offset
+// and a wave-uniform offset (scalar register), so no 64-bit per-lane addresses are kept.
+// Loads past the end return 0.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 __device__ inline float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Map a linear workgroup id to (query block, head) so that all query blocks of a head
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   xcd_map(blockIdx.x, gridDim.x, p.n_qblk, qb, bh);
   const int qi = qb * kBM + wave * 32 + col;  // this lane's query
   const bool q_ok = qi < p.n_q;
-  const float sl = p.s * kLog2e;
+  const float scale_l2 = p.s * kLog2e;  // softmax scale in log2 units
 
   // ---------------- query operands ----------------
   i32x4 qhi[KSTEPS], qlo[KSTEPS];  // int8 hi/lo of q_f (cached keys), or the bf16 query
@@ -268,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));  // stream-wide max
     const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
-    const float A = mxa > 0.f ? sl * (mxa / kQFix) : 0.f;
+    const float A = mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
     int qs = 0;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; kk++)
@@ -356,6 +363,13 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   const uint16_t* vz_base = p.v_zero + (size_t)bh * n_tot;
   const uint16_t* kr_base = p.k_cur + (size_t)bh * p.n_r * D;
   const uint16_t* vr_base = p.v_cur + (size_t)bh * p.n_r * D;
+  // descriptors of this head's cached window (the byte sizes fit 31 bits: checked on the host)
+  const __amdgpu_buffer_rsrc_t rs_kc = buffer_rsrc(kc_base, (uint32_t)(n_tot * KW * 4));
+  const __amdgpu_buffer_rsrc_t rs_vc = buffer_rsrc(vc_base, (uint32_t)(n_tot * VWT / kBN * 4));
+  const __amdgpu_buffer_rsrc_t rs_ks = buffer_rsrc(ks_base, (uint32_t)(n_tot * 2));
+  const __amdgpu_buffer_rsrc_t rs_kz = buffer_rsrc(kz_base, (uint32_t)(n_tot * 2));
+  const __amdgpu_buffer_rsrc_t rs_vs = buffer_rsrc(vs_base, (uint32_t)(n_tot * 2));
+  const __amdgpu_buffer_rsrc_t rs_vz = buffer_rsrc(vz_base, (uint32_t)(n_tot * 2));
   auto n_valid = [&](int U) KVQ_INLINE {
     return U < n_ct ? min(kBN, p.chunk_len - (U % tiles_per_chunk) * kBN) : min(kBN, p.n_r - (U - n_ct) * kBN);
   };
@@ -394,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));  // stream-wide max
     const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
-    a_ch = mxa > 0.f ? sl * (mxa / kQFix) : 0.f;
+    a_ch = mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
     float zs = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; kk++) {
@@ -441,29 +455,30 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
 
   auto load_k = [&](int U, auto k_c) KVQ_INLINE {
     if constexpr (decltype(k_c)::value == kCached) {
-      const size_t tok0 = (size_t)U * kBN;
+      // buffer loads: per-lane offsets are loop-invariant, the tile offset is uniform
+      const uint32_t tok0 = (uint32_t)U * kBN;
 #pragma unroll
       for (int i = 0; i < KUPT; i++) {
-        const int un = min(tid + i * kThreads, KUNITS - 1);
-        const uint32_t* src = kc_base + tok0 * KW + (size_t)un * KU;
+        const uint32_t un = (uint32_t)min(tid + i * kThreads, KUNITS - 1);
         if constexpr (KU == 2) {
-          const uint2 w = *reinterpret_cast<const uint2*>(src);
-          kpre[i].x = w.x;
-          kpre[i].y = w.y;
+          const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs_kc, un * 8u, tok0 * KW * 4u, 0);
+          kpre[i].x = w[0];
+          kpre[i].y = w[1];
         } else {
-          kpre[i].x = src[0];
+          kpre[i].x = __builtin_amdgcn_raw_buffer_load_b32(rs_kc, un * 4u, tok0 * KW * 4u, 0);
         }
       }
       if constexpr (!PERCH) {
-        pk_dk = ks_base[tok0 + (tid & (kBN - 1))];
-        pk_zk = kz_base[tok0 + (tid & (kBN - 1))];
+        const uint32_t j = (uint32_t)(tid & (kBN - 1));
+        pk_dk = __builtin_amdgcn_raw_buffer_load_b16(rs_ks, j * 2u, tok0 * 2u, 0);
+        pk_zk = __builtin_amdgcn_raw_buffer_load_b16(rs_kz, j * 2u, tok0 * 2u, 0);
       }
       if constexpr (!MASS_ONLY) {
-        const int g = (tid >> 3) & 3, j = tid & 7;
-        pz0 = vz_base[tok0 + 16 * g + j];
-        pz1 = vz_base[tok0 + 16 * g + j + 8];
-        pd0 = vs_base[tok0 + 16 * g + j];
-        pd1 = vs_base[tok0 + 16 * g + j + 8];
+        const uint32_t j = (uint32_t)(16 * ((tid >> 3) & 3) + (tid & 7));
+        pz0 = __builtin_amdgcn_raw_buffer_load_b16(rs_vz, j * 2u, tok0 * 2u, 0);
+        pz1 = __builtin_amdgcn_raw_buffer_load_b16(rs_vz, j * 2u + 16u, tok0 * 2u, 0);
+        pd0 = __builtin_amdgcn_raw_buffer_load_b16(rs_vs, j * 2u, tok0 * 2u, 0);
+        pd1 = __builtin_amdgcn_raw_buffer_load_b16(rs_vs, j * 2u + 16u, tok0 * 2u, 0);
       }
     } else {
       const int t0 = (U - n_ct) * kBN;
@@ -475,9 +490,9 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       }
     }
   };
-  auto store_k = [&](int U, auto k_c) KVQ_INLINE {
-    typename SM::KSlot& ks = sm.k[U % 3];
-    typename SM::PSlot& ps = sm.prm[U % 3];
+  auto store_k = [&](int U, int slot, auto k_c) KVQ_INLINE {
+    typename SM::KSlot& ks = sm.k[slot];
+    typename SM::PSlot& ps = sm.prm[slot];
     const int nv = n_valid(U);
     if constexpr (decltype(k_c)::value == kCached) {
 #pragma unroll
@@ -525,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       }
       if constexpr (!MASS_ONLY) {
         if (wave == 2 && lane < kBN / 2) {
-          typename SM::ZSlot& zs = sm.z[U % 3];
+          typename SM::ZSlot& zs = sm.z[slot];
           const int g = lane >> 3, j = lane & 7;
           const bool ok0 = 16 * g + j < nv, ok1 = 16 * g + j + 8 < nv;
           zs.zv[lane] = pack_f16x2(ok0 ? -1024.f - half_bits_to_f32(pz0) : -1024.f,
@@ -559,14 +574,13 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     if constexpr (decltype(k_c)::value == kCached) {
 #pragma unroll
       for (int i = 0; i < VGPT; i++) {
-        const int vg = min(tid + i * kThreads, VGROUPS - 1);
-        const uint32_t* src = vc_base + (size_t)U * VWT + (size_t)vg * WPG;
+        const uint32_t vg = (uint32_t)min(tid + i * kThreads, VGROUPS - 1);
         if constexpr (WPG == 2) {
-          const uint2 w = *reinterpret_cast<const uint2*>(src);
-          vpre[i].x = w.x;
-          vpre[i].y = w.y;
+          const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs_vc, vg * 8u, (uint32_t)U * VWT * 4u, 0);
+          vpre[i].x = w[0];
+          vpre[i].y = w[1];
         } else {
-          vpre[i].x = src[0];
+          vpre[i].x = __builtin_amdgcn_raw_buffer_load_b32(rs_vc, vg * 4u, (uint32_t)U * VWT * 4u, 0);
         }
       }
     } else {
@@ -582,11 +596,14 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       }
     }
   };
-  auto store_v = [&](int U, auto k_c) KVQ_INLINE {  // the pairs of tile U must be visible in sm.z[U % 3]
+  // the 2-bit field mask in a vector register lets the unpack use one and-or per pair
+  uint32_t vmask2 = 0x00030003u;
+  asm volatile("" : "+v"(vmask2));
+  auto store_v = [&](int U, int slot, auto k_c) KVQ_INLINE {  // the pairs of tile U must be visible in sm.z[slot]
     if constexpr (MASS_ONLY) return;
-    _Float16(*vrows)[SM::VROW] = sm.v[U % 3];
+    _Float16(*vrows)[SM::VROW] = sm.v[slot];
     if constexpr (decltype(k_c)::value == kCached) {
-      const typename SM::ZSlot& zs = sm.z[U % 3];
+      const typename SM::ZSlot& zs = sm.z[slot];
 #pragma unroll
       for (int i = 0; i < VGPT; i++) {
         const int vg = tid + i * kThreads;
@@ -602,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         if constexpr (BITS == 2) {
           const uint32_t w = vpre[i].x;
 #pragma unroll
-          for (int j = 0; j < 8; j++) a[j] = ((w >> (2 * j)) & 0x00030003u) | 0x64006400u;
+          for (int j = 0; j < 8; j++) a[j] = ((w >> (2 * j)) & vmask2) | 0x64006400u;
         } else {
           // t0 = [w0.b0 w0.b1 w1.b0 w1.b1], t1 = [w0.b2 w0.b3 w1.b2 w1.b3]
           const uint32_t w0 = vpre[i].x, w1 = vpre[i].y;
@@ -661,22 +678,31 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
 #pragma unroll
   for (int c = 0; c < CBLK; c++) acc[c] = f32x16{};
 
-  // QK^T and bias of block mb of tile U (kind K) into score set SET.
-  auto qk = [&](int U, int mb, auto set_c, auto k_c) KVQ_INLINE {
-    constexpr int SET = decltype(set_c)::value;
-    const typename SM::KSlot& ks = sm.k[U % 3];
-    const typename SM::PSlot& ps = sm.prm[U % 3];
+  // Key-side operands of block mb of tile U: the bias row and the key codes (cached) or
+  // bf16 key rows (current), read from LDS ahead of their MFMAs.
+  uint4 kbop;
+  i32x4 kop[D / 16];
+  auto read_k = [&](int slot, int mb, auto k_c) KVQ_INLINE {
+    const typename SM::KSlot& ks = sm.k[slot];
     const int krow = 32 * mb + mrow_key(col);
+    kbop = sm.prm[slot].kb[32 * mb + col][h];
+    if constexpr (decltype(k_c)::value == kCached) {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; kk++) kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < D / 16; t++) kop[t] = *reinterpret_cast<const i32x4*>(&ks.kr[krow][HALF * h + 8 * t]);
+    }
+  };
+  // QK^T and bias of the block whose operands read_k loaded, into score set SET.
+  auto qk = [&](auto set_c, auto k_c) KVQ_INLINE {
+    constexpr int SET = decltype(set_c)::value;
     {
-      const uint4 kb = ps.kb[32 * mb + col][h];
       const f32x16 zf = {};
-      cb[SET] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kb), qbias, zf, 0, 0, 0);
+      cb[SET] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kbop), qbias, zf, 0, 0, 0);
     }
     if constexpr (decltype(k_c)::value == kCached) {
       // S = 256 S_hi + S_lo in one accumulator: the hi sums, a shift, then the lo sums
-      i32x4 kop[KSTEPS];
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk++) kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
       i32x16 acc_s = {};
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; kk++) acc_s = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[kk], qhi[kk], acc_s, 0, 0, 0);
@@ -689,7 +715,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
 #pragma unroll
       for (int t = 0; t < D / 16; t++) {
         const bf16x8 qop = __builtin_bit_cast(bf16x8, t < KSTEPS ? qhi[t] : qlo[t - KSTEPS]);
-        const bf16x8 aop = *reinterpret_cast<const bf16x8*>(&ks.kr[krow][HALF * h + 8 * t]);
+        const bf16x8 aop = __builtin_bit_cast(bf16x8, kop[t]);
         if (t == 0) {
           const f32x16 z = {};
           sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, qop, z, 0, 0, 0);
@@ -700,29 +726,37 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       sqh[SET] = __builtin_bit_cast(i32x16, sc);
     }
   };
-  // PV of block mb of tile U with the pairs in pb.
-  auto pv = [&](int U, int mb) KVQ_INLINE {
+  // Value operands of block mb of tile U, read from LDS ahead of the PV MFMAs.
+  f16x8 vop[2][CBLK];
+  auto read_v = [&](int slot, int mb) KVQ_INLINE {
     if constexpr (!MASS_ONLY) {
-      const _Float16(*vrows)[SM::VROW] = sm.v[U % 3];
+      const _Float16(*vrows)[SM::VROW] = sm.v[slot];
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int c = 0; c < CBLK; c++)
+          vop[ks][c] = *reinterpret_cast<const f16x8*>(&vrows[32 * c + col][32 * mb + 16 * ks + 8 * h]);
+    }
+  };
+  // PV of the block whose values read_v loaded, with the pairs in pb.
+  auto pv = [&]() KVQ_INLINE {
+    if constexpr (!MASS_ONLY) {
 #pragma unroll
       for (int ks = 0; ks < 2; ks++) {
         const f16x8 bop = __builtin_bit_cast(f16x8, make_uint4(pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]));
 #pragma unroll
-        for (int c = 0; c < CBLK; c++) {
-          const f16x8 aop = *reinterpret_cast<const f16x8*>(&vrows[32 * c + col][32 * mb + 16 * ks + 8 * h]);
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aop, bop, acc[c], 0, 0, 0);
-        }
+        for (int c = 0; c < CBLK; c++) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[ks][c], bop, acc[c], 0, 0, 0);
       }
     }
   };
   // Logits (log2 units; they carry -m through the bias) of block mb of tile U from SET.
-  auto logits = [&](int U, int mb, auto set_c, auto k_c, float* x) KVQ_INLINE {
+  auto logits = [&](int slot, int mb, auto set_c, auto k_c, float* x) KVQ_INLINE {
     constexpr int SET = decltype(set_c)::value;
     if constexpr (decltype(k_c)::value == kCached && PERCH) {
 #pragma unroll
       for (int v = 0; v < 16; v++) x[v] = fmaf(a_ch, (float)sqh[SET][v], cb[SET][v]);
     } else if constexpr (decltype(k_c)::value == kCached) {
-      const float* dka = sm.prm[U % 3].dka[wave];
+      const float* dka = sm.prm[slot].dka[wave];
 #pragma unroll
       for (int v4 = 0; v4 < 4; v4++) {
         const float4 d4 = *reinterpret_cast<const float4*>(&dka[32 * mb + 8 * v4 + 4 * h]);
@@ -735,7 +769,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       }
     } else {
 #pragma unroll
-      for (int v = 0; v < 16; v++) x[v] = fmaf(sl, __int_as_float(sqh[SET][v]), cb[SET][v]);
+      for (int v = 0; v < 16; v++) x[v] = fmaf(scale_l2, __int_as_float(sqh[SET][v]), cb[SET][v]);
     }
   };
   // fp16 P pairs with p = exp2(x - off) into pb; returns this lane's fp16 sum.
@@ -755,9 +789,9 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   // only when a block's fp16 row sum passes 2^15 (some p may have left the fp16 range):
   // then m becomes that block's maximum, the sums and the accumulator are rescaled and
   // the block's p recomputed (a rare, wave-uniform branch).
-  auto softmax = [&](int U, int mb, auto set_c, auto k_c, auto first_c) KVQ_INLINE {
+  auto softmax = [&](int slot, int mb, auto set_c, auto k_c, auto first_c) KVQ_INLINE {
     float x[16];
-    logits(U, mb, set_c, k_c, x);
+    logits(slot, mb, set_c, k_c, x);
     float lsum = 0.f;
     bool done = false;
     if constexpr (decltype(first_c)::value) {
@@ -841,10 +875,11 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       for (int v = 0; v < 16; v++) acc[c][v] *= cn;
   };
 
-  // Step T of a run of n_t tiles of one kind (tile index U = U0 + T): QK^T, softmax and
-  // PV of the tile's two 32-key blocks, while the keys of tile U+2 and the values of
-  // tile U+1 are staged. FIRST: block (U,0) may be the stream's first.
-  auto step = [&](int U0, int n_t, int T, auto k_c, auto first_c) KVQ_INLINE {
+  // Step T of a run of n_t tiles of one kind (tile index U = U0 + T in LDS slot slot0;
+  // the next two tiles in slots slot1, slot2): QK^T, softmax and PV of the tile's two 32-key
+  // blocks, while the keys of tile U+2 and the values of tile U+1 are staged. FIRST:
+  // block (U,0) may be the stream's first.
+  auto step = [&](int U0, int n_t, int T, int slot0, int slot1, int slot2, auto k_c, auto first_c) KVQ_INLINE {
     const Kind<0> set0;
     const std::false_type no;
     const int U = U0 + T;
@@ -854,32 +889,50 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     if constexpr (PERCH && decltype(k_c)::value == kCached) {
       if ((U % tiles_per_chunk) % k_tpg == 0) refresh_group(U);
     }
-    qk(U, 0, set0, k_c);
-    softmax(U, 0, set0, k_c, first_c);
-    pv(U, 0);
-    qk(U, 1, set0, k_c);
-    softmax(U, 1, set0, k_c, no);
-    pv(U, 1);
-    if (stage_k) store_k(U + 2, k_c);
-    if (stage_v) store_v(U + 1, k_c);
+    // operand reads are issued one phase ahead of their MFMAs (the sched barriers keep
+    // the compiler from sinking them): values under the softmax, keys under the PV
+    read_k(slot0, 0, k_c);
+    qk(set0, k_c);
+    read_v(slot0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(slot0, 0, set0, k_c, first_c);
+    read_k(slot0, 1, k_c);
+    __builtin_amdgcn_sched_barrier(0);
+    pv();
+    qk(set0, k_c);
+    read_v(slot0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // the key staging (VALU and LDS writes) runs in the shadow of block 1's QK^T MFMAs
+    if (stage_k) store_k(U + 2, slot2, k_c);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(slot0, 1, set0, k_c, no);
+    pv();
+    if (stage_v) store_v(U + 1, slot1, k_c);
     __syncthreads();
   };
-  // All tiles of one kind: stage the first two tiles' keys and the first values, then
-  // run the steps.
+  // All tiles of one kind (tile U0 + T in slot T mod 3, the slots rotating with T): stage
+  // the first two tiles' keys and the first values, then run the steps.
   auto run = [&](int U0, int n_t, auto k_c) KVQ_INLINE {
     const std::false_type no;
     load_k(U0, k_c);
-    store_k(U0, k_c);
+    store_k(U0, 0, k_c);
     if (n_t > 1) {
       load_k(U0 + 1, k_c);
-      store_k(U0 + 1, k_c);
+      store_k(U0 + 1, 1, k_c);
     }
     __syncthreads();
     load_v(U0, k_c);
-    store_v(U0, k_c);
+    store_v(U0, 0, k_c);
     __syncthreads();
-    step(U0, n_t, 0, k_c, std::true_type());
-    for (int T = 1; T < n_t; T++) step(U0, n_t, T, k_c, no);
+    step(U0, n_t, 0, 0, 1, 2, k_c, std::true_type());
+    int s0 = 1, s1 = 2, s2 = 0;
+    for (int T = 1; T < n_t; T++) {
+      step(U0, n_t, T, s0, s1, s2, k_c, no);
+      const int t = s0;
+      s0 = s1;
+      s1 = s2;
+      s2 = t;
+    }
   };
 
   // ---------------- the cached window, then the current chunk ----------------
@@ -938,6 +991,8 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
     return KVQ_ERR_SHAPE;
   if ((long long)a->n_chunks * a->chunk_len + a->n_r < 1) return KVQ_ERR_SHAPE;
   if (!(a->softmax_scale >= 0.f) || isinf(a->softmax_scale)) return KVQ_ERR_SHAPE;
+  // the kernel addresses one head's cached codes through 32-bit buffer offsets
+  if ((long long)a->n_chunks * chunk_pad(a->chunk_len) * a->d * kf.bits / 8 > 0x7FFFFFFFLL) return KVQ_ERR_SHAPE;
   const long long nqblk = (a->n_q + kBM - 1) / kBM;
   if (nqblk * a->B * a->H > 0x7FFFFFFFLL) return KVQ_ERR_SHAPE;
   if (!a->q) return KVQ_ERR_NULL;

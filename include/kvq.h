@@ -146,8 +146,9 @@ typedef struct {
  * leave the fp16 range), values fp16((code - z) Delta); sums and outputs fp32.
  * Preconditions on the data (not checked): key steps Delta < 2048 and |Delta z| < 65504
  * (per token), scaled logits |s q.k| and the correction below 2^15 nats.
- * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED (mixed bits, value per-channel,
- * wrong roles, group not 64/128), KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
+ * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (also when one head's cached codes exceed 2^31 - 1
+ * bytes), KVQ_ERR_UNSUPPORTED (mixed bits, value per-channel, wrong roles, group not
+ * 64/128), KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
 int jb_attn_fwd(const jb_attn_args* a, void* stream);
 
 /* Attention masses only (Fig. 2): writes mass_s and mass_r; o and values are not read. */

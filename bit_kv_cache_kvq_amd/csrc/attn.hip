@@ -200,12 +200,16 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   constexpr int VITEMS = (kBN / 2) * SEGS;  // current-value (token pair, segment) items per tile
   // items per thread (work counts below kThreads leave whole waves idle)
   constexpr int KUPT = (KUNITS + kThreads - 1) / kThreads;
-  constexpr int VGPT = (VGROUPS + kThreads - 1) / kThreads;
+  // Cached values are staged by the first wave of each SIMD only (waves 0..3): the second
+  // wave of a SIMD issues after the first and is the one that ends each step last.
+  constexpr int kVST = kThreads / 2;
+  constexpr int VGPT = (VGROUPS + kVST - 1) / kVST;
   constexpr int RIPT = (RITEMS + kThreads - 1) / kThreads;
   constexpr int VRPT = (VITEMS + kThreads - 1) / kThreads;
   static_assert(kStreams == 1, "one 32-query stream per wave");
   static_assert(KUNITS % 64 == 0 && VGROUPS % 64 == 0 && RITEMS % 64 == 0 && VITEMS % 64 == 0, "wave-uniform split");
   static_assert(KUPT <= RIPT && VGPT <= 2 * VRPT && RIPT <= 4 && VRPT <= 2, "staging registers");
+  static_assert(kVST % 64 == 0 && kVST % 4 == 0, "value staging by whole waves, one token group per lane");
   __shared__ SM sm;
 
   const int tid = threadIdx.x;
@@ -572,9 +576,10 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   auto load_v = [&](int U, auto k_c) KVQ_INLINE {
     if constexpr (MASS_ONLY) return;
     if constexpr (decltype(k_c)::value == kCached) {
+      if (tid >= kVST) return;
 #pragma unroll
       for (int i = 0; i < VGPT; i++) {
-        const uint32_t vg = (uint32_t)min(tid + i * kThreads, VGROUPS - 1);
+        const uint32_t vg = (uint32_t)min(tid + i * kVST, VGROUPS - 1);
         if constexpr (WPG == 2) {
           const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs_vc, vg * 8u, (uint32_t)U * VWT * 4u, 0);
           vpre[i].x = w[0];
@@ -603,18 +608,21 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     if constexpr (MASS_ONLY) return;
     _Float16(*vrows)[SM::VROW] = sm.v[slot];
     if constexpr (decltype(k_c)::value == kCached) {
+      if (tid >= kVST) return;
       const typename SM::ZSlot& zs = sm.z[slot];
+      // every group of this lane has the same token group g = tid mod 4 (kVST % 4 == 0)
+      const int g = tid & 3;
+      const uint4 z0 = *reinterpret_cast<const uint4*>(&zs.zv[8 * g]);
+      const uint4 z1 = *reinterpret_cast<const uint4*>(&zs.zv[8 * g + 4]);
+      const uint4 d0 = *reinterpret_cast<const uint4*>(&zs.dvp[8 * g]);
+      const uint4 d1 = *reinterpret_cast<const uint4*>(&zs.dvp[8 * g + 4]);
+      const uint32_t zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+      const uint32_t dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
 #pragma unroll
       for (int i = 0; i < VGPT; i++) {
-        const int vg = tid + i * kThreads;
-        if (VGROUPS % kThreads != 0 && vg >= VGROUPS) break;
-        const int ch = vg >> 2, g = vg & 3;  // 16-token group g of channel ch
-        const uint4 z0 = *reinterpret_cast<const uint4*>(&zs.zv[8 * g]);
-        const uint4 z1 = *reinterpret_cast<const uint4*>(&zs.zv[8 * g + 4]);
-        const uint4 d0 = *reinterpret_cast<const uint4*>(&zs.dvp[8 * g]);
-        const uint4 d1 = *reinterpret_cast<const uint4*>(&zs.dvp[8 * g + 4]);
-        const uint32_t zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-        const uint32_t dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        const int vg = tid + i * kVST;
+        if (VGROUPS % kVST != 0 && vg >= VGROUPS) break;
+        const int ch = vg >> 2;  // 16-token group g of channel ch
         uint32_t a[8];
         if constexpr (BITS == 2) {
           const uint32_t w = vpre[i].x;

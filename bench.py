@@ -134,6 +134,7 @@ def main():
     vnext = kvq.alloc_window(vf, w.B, w.H, w.d, w.n_r, 1)
     a = kvq.make_args(q, kr, vr, kwin, vwin, w.chunk_len, w.n_chunks, kf, vf, o=o, mass_s=ms, mass_r=mr,
                       correction=args.correction)
+    ws = kvq.attach_workspace(a)  # split-window partials when the grid is small for the device
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -183,7 +184,7 @@ def main():
                                f"{w.n_chunks}x{w.chunk_len} cached tokens, INT{w.bits} per-{w.k_granularity} K, "
                                f"per-token V, Hadamard, correction={'taylor' if args.correction else 'none'}",
                    "B": w.B, "H": w.H, "d": w.d, "n_q": w.n_q, "n_c": w.n_c, "bits": w.bits,
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)", "split_workspace_bytes": a.workspace_bytes},
         "attn_ms": round(attn_ms, 4),
         "cache_GBps": round(cache_bytes / (attn_ms * 1e-3) / 1e9, 2),
         "cache_frac_hbm": round(cache_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),

@@ -91,6 +91,8 @@ struct Params {
   int correction;
   int k_had, v_had;
   int k_group;  // tokens per key channel group (per-channel keys), else 0
+  int n_split;  // workgroups per query block, each over a contiguous share of the tiles
+  float* part;  // n_split > 1: partial records [n_split][B*H][n_q][D + 4], else null
   float* o;
   float* mass_s;
   float* mass_r;
@@ -215,8 +217,9 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
-  int qb, bh;
-  xcd_map(blockIdx.x, gridDim.x, p.n_qblk, qb, bh);
+  int qbs, bh;
+  xcd_map(blockIdx.x, gridDim.x, p.n_qblk * p.n_split, qbs, bh);
+  const int qb = qbs / p.n_split, sp = qbs % p.n_split;  // query block, share of the tiles
   const int qi = qb * kBM + wave * 32 + col;  // this lane's query
   const bool q_ok = qi < p.n_q;
   const float scale_l2 = p.s * kLog2e;  // softmax scale in log2 units
@@ -895,7 +898,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     if (stage_k) load_k(U + 2, k_c);
     if (stage_v) load_v(U + 1, k_c);
     if constexpr (PERCH && decltype(k_c)::value == kCached) {
-      if ((U % tiles_per_chunk) % k_tpg == 0) refresh_group(U);
+      if (T == 0 || (U % tiles_per_chunk) % k_tpg == 0) refresh_group(U);
     }
     // operand reads are issued one phase ahead of their MFMAs (the sched barriers keep
     // the compiler from sinking them): values under the softmax, keys under the PV
@@ -943,20 +946,25 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     }
   };
 
-  // ---------------- the cached window, then the current chunk ----------------
-  if (n_ct > 0) {
-    run(0, n_ct, Kind<kCached>());
+  // ---------------- this workgroup's tiles: cached ones, then current ones ----------------
+  // Share sp of the tile sequence (cached tiles 0..n_ct-1, then the current chunk's).
+  const int n_tt = n_ct + n_rt;
+  const int t_beg = (int)((long long)sp * n_tt / p.n_split), t_end = (int)((long long)(sp + 1) * n_tt / p.n_split);
+  const int c_beg = min(t_beg, n_ct), c_end = min(t_end, n_ct);
+  const int r_beg = max(t_beg, n_ct) - n_ct, r_end = max(t_end, n_ct) - n_ct;
+  if (c_end > c_beg) {
+    run(c_beg, c_end - c_beg, Kind<kCached>());
     if constexpr (!MASS_ONLY) {
       if (p.v_had) unrotate();
     }
   }
-  if (n_rt > 0) {
+  if (r_end > r_beg) {
     load_query_bf16();
     if constexpr (PERCH) {
       c_grp = 0.f;
       write_mslot();
     }
-    run(n_ct, n_rt, Kind<kCurrent>());
+    run(n_ct + r_beg, r_end - r_beg, Kind<kCurrent>());
   }
 
   // ---------------- epilogue ----------------
@@ -964,6 +972,20 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   const float lr = l_r + xor32(l_r);
   const float tot = ls + lr;
   if (!q_ok) return;
+  if (p.part) {
+    // partial record of this share: the unnormalized sum, its reference max and the sums
+    float* rec = p.part + (((size_t)sp * p.B * p.H + bh) * p.n_q + qi) * (D + 4);
+    if constexpr (!MASS_ONLY) {
+#pragma unroll
+      for (int c = 0; c < CBLK; c++)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; v4++)
+          *reinterpret_cast<float4*>(rec + 32 * c + 8 * v4 + 4 * h) =
+              make_float4(acc[c][4 * v4], acc[c][4 * v4 + 1], acc[c][4 * v4 + 2], acc[c][4 * v4 + 3]);
+    }
+    if (h == 0) *reinterpret_cast<float4*>(rec + D) = make_float4(m_run, ls, lr, 0.f);
+    return;
+  }
   const float inv = 1.f / tot;
   if (!MASS_ONLY) {
     float* orow = p.o + ((size_t)bh * p.n_q + qi) * D;
@@ -1024,8 +1046,86 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   return KVQ_OK;
 }
 
+// Combines the partial records of the n_split shares of each query: with M the largest
+// reference max, weights w = 2^(m - M); O = sum w acc / sum w (l_S + l_R), and the
+// masses from the weighted sums. One thread per (query, 4 output channels); G threads
+// per query (G = 1 for masses only).
+template <int D, int G, bool MASS_ONLY>
+__global__ __launch_bounds__(256) void jb_combine_kernel(const float* __restrict__ part, int n_split, size_t rows,
+                                                         float* __restrict__ o, float* __restrict__ mass_s,
+                                                         float* __restrict__ mass_r) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = t / G;
+  const int cg = (int)(t % G);
+  if (row >= rows) return;
+  const size_t stride = rows * (D + 4);
+  const float* rec0 = part + row * (D + 4);
+  float M = -INFINITY;
+  for (int sp = 0; sp < n_split; sp++) M = fmaxf(M, rec0[sp * stride + D]);
+  float ls = 0.f, lr = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < n_split; sp++) {
+    const float* rec = rec0 + sp * stride;
+    const float4 st = *reinterpret_cast<const float4*>(rec + D);
+    const float w = exp2f(st.x - M);
+    ls = fmaf(w, st.y, ls);
+    lr = fmaf(w, st.z, lr);
+    if constexpr (!MASS_ONLY) {
+      const float4 v = *reinterpret_cast<const float4*>(rec + 4 * cg);
+      a.x = fmaf(w, v.x, a.x);
+      a.y = fmaf(w, v.y, a.y);
+      a.z = fmaf(w, v.z, a.z);
+      a.w = fmaf(w, v.w, a.w);
+    }
+  }
+  const float inv = 1.f / (ls + lr);
+  if constexpr (!MASS_ONLY)
+    *reinterpret_cast<float4*>(o + row * D + 4 * cg) = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+  if (cg == 0 && mass_s) {
+    mass_s[row] = ls * inv;
+    mass_r[row] = lr * inv;
+  }
+}
+
+struct AttnPlan {
+  int n_qblk, n_split;
+  size_t part_bytes;  // workspace the split needs (0 for n_split == 1)
+};
+
+// Splits each query block's tile sequence over n_split workgroups when that shortens the
+// critical path: with C compute units and one workgroup per unit at a time, a grid of g
+// workgroups over T tiles takes about ceil(g S / C) rounds of ceil(T / S) tiles. A split
+// is taken only for a gain of at least 10% (the partials cost a combine pass).
+AttnPlan plan_attn(const jb_attn_args* a) {
+  AttnPlan pl;
+  pl.n_qblk = (a->n_q + kBM - 1) / kBM;
+  pl.n_split = 1;
+  pl.part_bytes = 0;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1) {
+    (void)hipGetLastError();
+    return pl;
+  }
+  const long long grid = (long long)pl.n_qblk * a->B * a->H;
+  const long long tiles = (long long)a->n_chunks * (chunk_pad(a->chunk_len) / kBN) + (a->n_r + kBN - 1) / kBN;
+  auto cost = [&](long long S) { return ((grid * S + cus - 1) / cus) * ((tiles + S - 1) / S); };
+  long long best = cost(1);
+  for (int S = 2; S <= 8 && S <= tiles; S++) {
+    if (grid * S > 0x7FFFFFFFLL) break;
+    const long long c = cost(S);
+    if (10 * c <= 9 * best) {
+      best = c;
+      pl.n_split = S;
+    }
+  }
+  if (pl.n_split > 1)
+    pl.part_bytes = (size_t)pl.n_split * a->B * a->H * a->n_q * (size_t)(a->d + 4) * sizeof(float);
+  return pl;
+}
+
 template <int D, int BITS, bool MASS_ONLY, bool PERCH>
-int launch_attn(const jb_attn_args* a, hipStream_t st) {
+int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   Params p;
   p.B = a->B;
   p.H = a->H;
@@ -1034,7 +1134,7 @@ int launch_attn(const jb_attn_args* a, hipStream_t st) {
   p.chunk_len = a->chunk_len;
   p.n_chunks = a->n_chunks;
   p.cp = chunk_pad(a->chunk_len);
-  p.n_qblk = (a->n_q + kBM - 1) / kBM;
+  p.n_qblk = pl.n_qblk;
   p.q = a->q;
   p.k_cur = a->k_cur;
   p.v_cur = a->v_cur;
@@ -1049,11 +1149,19 @@ int launch_attn(const jb_attn_args* a, hipStream_t st) {
   p.k_had = a->k_fmt.hadamard;
   p.v_had = a->v_fmt.hadamard;
   p.k_group = PERCH ? a->k_fmt.group : 0;
+  p.n_split = pl.n_split;
+  p.part = pl.n_split > 1 ? static_cast<float*>(a->workspace) : nullptr;
   p.o = MASS_ONLY ? nullptr : a->o;
   p.mass_s = a->mass_s;
   p.mass_r = a->mass_r;
-  const unsigned grid = (unsigned)(p.n_qblk * a->B * a->H);
+  const unsigned grid = (unsigned)(pl.n_qblk * a->B * a->H * pl.n_split);
   jb_attn_kernel<D, BITS, MASS_ONLY, PERCH><<<grid, kThreads, 0, st>>>(p);
+  if (pl.n_split > 1) {
+    const size_t rows = (size_t)a->B * a->H * a->n_q;
+    constexpr int G = MASS_ONLY ? 1 : D / 4;
+    const unsigned cgrid = (unsigned)((rows * G + 255) / 256);
+    jb_combine_kernel<D, G, MASS_ONLY><<<cgrid, 256, 0, st>>>(p.part, pl.n_split, rows, p.o, p.mass_s, p.mass_r);
+  }
   return launch_status();
 }
 
@@ -1061,16 +1169,20 @@ template <bool MASS_ONLY>
 int dispatch(const jb_attn_args* a, void* stream) {
   const int st = validate_attn(a, MASS_ONLY);
   if (st) return st;
+  AttnPlan pl = plan_attn(a);
+  // without a workspace large enough for the partials the call runs unsplit
+  if (pl.n_split > 1 && (!a->workspace || a->workspace_bytes < pl.part_bytes)) pl.n_split = 1;
+  if (pl.n_split > 1 && !aligned16(a->workspace)) return KVQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool perch = a->k_fmt.granularity == KVQ_PER_CHANNEL;
   if (a->d == 128) {
     if (a->k_fmt.bits == 2)
-      return perch ? launch_attn<128, 2, MASS_ONLY, true>(a, s) : launch_attn<128, 2, MASS_ONLY, false>(a, s);
-    return perch ? launch_attn<128, 4, MASS_ONLY, true>(a, s) : launch_attn<128, 4, MASS_ONLY, false>(a, s);
+      return perch ? launch_attn<128, 2, MASS_ONLY, true>(a, pl, s) : launch_attn<128, 2, MASS_ONLY, false>(a, pl, s);
+    return perch ? launch_attn<128, 4, MASS_ONLY, true>(a, pl, s) : launch_attn<128, 4, MASS_ONLY, false>(a, pl, s);
   }
   if (a->k_fmt.bits == 2)
-    return perch ? launch_attn<64, 2, MASS_ONLY, true>(a, s) : launch_attn<64, 2, MASS_ONLY, false>(a, s);
-  return perch ? launch_attn<64, 4, MASS_ONLY, true>(a, s) : launch_attn<64, 4, MASS_ONLY, false>(a, s);
+    return perch ? launch_attn<64, 2, MASS_ONLY, true>(a, pl, s) : launch_attn<64, 2, MASS_ONLY, false>(a, pl, s);
+  return perch ? launch_attn<64, 4, MASS_ONLY, true>(a, pl, s) : launch_attn<64, 4, MASS_ONLY, false>(a, pl, s);
 }
 
 }  // namespace
@@ -1081,6 +1193,6 @@ extern "C" int jb_attn_fwd(const jb_attn_args* a, void* stream) { return kvq::di
 extern "C" int jb_attn_mass(const jb_attn_args* a, void* stream) { return kvq::dispatch<true>(a, stream); }
 
 extern "C" size_t jb_attn_workspace_bytes(const jb_attn_args* a) {
-  (void)a;
-  return 0;
+  if (kvq::validate_attn(a, false) != KVQ_OK && kvq::validate_attn(a, true) != KVQ_OK) return 0;
+  return kvq::plan_attn(a).part_bytes;
 }

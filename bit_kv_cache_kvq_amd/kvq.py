@@ -152,7 +152,9 @@ def kvq_pack(x, fmt: KvqFormat, n_chunks: int, chunk_idx: int, codes, scale, zer
 
 def make_args(q, k_cur, v_cur, k_window, v_window, chunk_len, n_chunks, k_fmt, v_fmt, o=None, mass_s=None,
               mass_r=None, correction=JB_CORR_TAYLOR, softmax_scale=0.0):
-    """Fill a JbAttnArgs from tensors. k_window / v_window are (codes, scale, zero) or None."""
+    """Fill a JbAttnArgs from tensors. k_window / v_window are (codes, scale, zero) or None.
+
+    The workspace is left empty (the call then runs unsplit); attach_workspace adds it."""
     B, H, n_q, d = q.shape
     n_r = k_cur.shape[2] if k_cur is not None else 0
     kw = k_window if k_window is not None else (None, None, None)
@@ -175,6 +177,19 @@ def jb_attn_mass(args: JbAttnArgs, stream=None):
 
 def jb_attn_workspace_bytes(args: JbAttnArgs) -> int:
     return int(_lib.jb_attn_workspace_bytes(ctypes.byref(args)))
+
+
+def attach_workspace(args: JbAttnArgs, device="cuda"):
+    """Allocate the split-window workspace the library asks for on the current device and
+    point args at it. Returns the tensor (None when no split is planned); it must stay
+    alive while calls made with args are in flight."""
+    n = jb_attn_workspace_bytes(args)
+    if n == 0:
+        args.workspace, args.workspace_bytes = None, 0
+        return None
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    args.workspace, args.workspace_bytes = ctypes.c_void_p(ws.data_ptr()), n
+    return ws
 
 
 def pack_window(x, chunk_len: int, fmt: KvqFormat, stream=None):

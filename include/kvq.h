@@ -135,8 +135,8 @@ typedef struct {
   float* o;                   /* fp32 [B, H, n_q, d]: required by fwd, ignored by mass */
   float* mass_s;              /* fp32 [B, H, n_q]: optional in fwd (NULL), required in mass */
   float* mass_r;              /* fp32 [B, H, n_q]: as mass_s */
-  void* workspace;            /* reserved for split-window partials; may be NULL */
-  size_t workspace_bytes;
+  void* workspace;            /* device, 16-byte aligned, caller-owned; may be NULL (see below) */
+  size_t workspace_bytes;     /* its size in bytes */
 } jb_attn_args;
 
 /* Corrected attention forward: writes o and, if given, mass_s/mass_r.
@@ -148,13 +148,22 @@ typedef struct {
  * (per token), scaled logits |s q.k| and the correction below 2^15 nats.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (also when one head's cached codes exceed 2^31 - 1
  * bytes), KVQ_ERR_UNSUPPORTED (mixed bits, value per-channel, wrong roles, group not
- * 64/128), KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
+ * 64/128), KVQ_ERR_ALIGN (also a misaligned workspace that a split would use), KVQ_ERR_HIP. */
 int jb_attn_fwd(const jb_attn_args* a, void* stream);
 
 /* Attention masses only (Fig. 2): writes mass_s and mass_r; o and values are not read. */
 int jb_attn_mass(const jb_attn_args* a, void* stream);
 
-/* Workspace bytes the call would use (0: none needed). */
+/* Workspace bytes a call with these arguments uses on the current device (0: none).
+ * When the grid of query blocks is small for the device (fewer workgroups than its compute
+ * units can take in whole rounds), the call splits each query block's tiles (cached
+ * window, then current chunk) into up to 8 contiguous shares, one workgroup each, writes
+ * one partial record per share and query (unnormalized sum, reference max, l_S, l_R:
+ * fp32 [shares][B*H][n_q][d + 4]) into the workspace and combines them in a second kernel
+ * on the same stream. A call given no workspace, or one smaller than this size, runs
+ * unsplit; the two differ by rounding only (each share takes its fp16 numerators
+ * relative to its own reference max). The workspace must not be shared by calls that may
+ * run concurrently. Returns 0 for invalid arguments. */
 size_t jb_attn_workspace_bytes(const jb_attn_args* a);
 
 /* Static description of a status code. */

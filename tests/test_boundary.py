@@ -109,4 +109,4 @@ def test_attn_validation_without_launch(kvq):
     assert fwd(args(q=P + 2)) == -4
     assert fwd(args(softmax_scale=-1.0)) == -2
     assert mass(args()) == -1                   # mass needs mass_s / mass_r
-    assert lib.jb_attn_workspace_bytes(ctypes.byref(args())) == 0
+    assert lib.jb_attn_workspace_bytes(ctypes.byref(args())) == 0   # no device here: no split planned

@@ -127,3 +127,15 @@ def test_correction_restores_attention_mass(name, nrows):
 def test_correction_restores_attention_mass_long_window():
     unc, cor, improved, shift = _mass_stat("long", 64)
     assert shift > 0 and cor < unc and improved > 0.6
+
+
+def test_mass_check_heavy_tailed_per_channel_keys_reported():
+    # Config 4 (Student-t(3) keys quantized per channel): the uniform rounding-noise model
+    # behind the correction overstates the error variance of heavy-tailed channels (most
+    # values sit near a grid point, the tails set the step), so the mass check is reported
+    # here rather than asserted; its direction is a property of the data.
+    unc, cor, improved, shift = _mass_stat("c40_perch", 128)
+    print(f"[P9 c40_perch] |P_S unc - bf16| {unc:.4f}  |P_S corr - bf16| {cor:.4f}  rows improved {improved:.2f}  "
+          f"mean shift {shift:+.4f}", flush=True)
+    assert np.isfinite([unc, cor, improved, shift]).all()
+    assert 0.0 <= improved <= 1.0

@@ -145,11 +145,13 @@ def main():
             ev[1].record(stream)
         kvq.kvq_pack(kr, kf, 1, 0, *knext, stream)
         kvq.kvq_pack(vr, vf, 1, 0, *vnext, stream)
+        if ev is not None:
+            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -157,7 +159,11 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = float(np.mean([e0.elapsed_time(e1) for (e0, e1) in evs]))
+    attn_ms = float(np.mean([e0.elapsed_time(e1) for (e0, e1, _) in evs]))
+    pack_ms = float(np.mean([e1.elapsed_time(e2) for (_, e1, e2) in evs]))
+    # algorithmic bytes of the two packs: the chunk's bf16 keys and values read once, their
+    # codes, steps and zero points written once
+    pack_bytes = 2 * w.bh * w.n_r * w.d * 2 + sum(t.numel() * t.element_size() for t in (*knext, *vnext))
 
     flops = w.flops()
     cache_bytes = (kwin[0].numel() * 4 + kwin[1].numel() * 2 * 2 + vwin[0].numel() * 4 + vwin[1].numel() * 2 * 2)
@@ -188,6 +194,9 @@ def main():
         "attn_ms": round(attn_ms, 4),
         "cache_GBps": round(cache_bytes / (attn_ms * 1e-3) / 1e9, 2),
         "cache_frac_hbm": round(cache_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+        "pack": {"ms": round(pack_ms, 4), "algorithmic_bytes": pack_bytes,
+                 "GBps": round(pack_bytes / (pack_ms * 1e-3) / 1e9, 1),
+                 "frac_hbm": round(pack_bytes / (pack_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
                      "traffic": (round(traffic) if traffic is not None else None),

@@ -60,6 +60,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -93,6 +94,7 @@ struct Params {
   int k_group;  // tokens per key channel group (per-channel keys), else 0
   int n_split;  // workgroups per query block, each over a contiguous share of the tiles
   float* part;  // n_split > 1: partial records [n_split][B*H][n_q][D + 4], else null
+  const float* qrot;  // per-channel rotated keys: H q / sqrt(d) fp32 [B*H][n_q][D], else null
   float* o;
   float* mass_s;
   float* mass_r;
@@ -396,7 +398,19 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     const uint4* drow = reinterpret_cast<const uint4*>(p.k_scale + prow);
     const uint4* zrow = reinterpret_cast<const uint4*>(p.k_zero + prow);
     float qv[HALF];
-    rotated_query(qv);
+    if (p.qrot) {  // rotated once for the whole call by jb_rotate_q_kernel
+      const float4* src = reinterpret_cast<const float4*>(p.qrot + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h);
+#pragma unroll
+      for (int u = 0; u < HALF / 4; u++) {
+        const float4 v = src[u];
+        qv[4 * u] = v.x;
+        qv[4 * u + 1] = v.y;
+        qv[4 * u + 2] = v.z;
+        qv[4 * u + 3] = v.w;
+      }
+    } else {
+      rotated_query(qv);
+    }
     float ss = 0.f, mxa = 0.f;
 #pragma unroll
     for (int u = 0; u < HALF / 8; u++) {
@@ -404,10 +418,11 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        const float dl = half_bits_to_f32(e & 1 ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu);
-        const float qt = qv[8 * u + e] * dl;
+        // the fp16 step enters a mixed-precision fma (no separate conversion)
+        const f16x2 d2 = __builtin_bit_cast(f16x2, ww[e >> 1]);
+        const float qt = fmaf(qv[8 * u + e], (float)d2[e & 1], 0.f);
         qv[8 * u + e] = qt;
-        ss += qt * qt;
+        ss = fmaf(qt, qt, ss);
         mxa = fmaxf(mxa, fabsf(qt));
       }
     }
@@ -419,29 +434,31 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     float zs = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; kk++) {
-      float zt[16];
+      _Float16 zt[16];
 #pragma unroll
       for (int u2 = 0; u2 < 2; u2++) {
         const uint4 w = zrow[2 * kk + u2];
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int e = 0; e < 8; e++) zt[8 * u2 + e] = half_bits_to_f32(e & 1 ? ww[e >> 1] >> 16 : ww[e >> 1] & 0xFFFFu);
+        for (int e = 0; e < 8; e++) zt[8 * u2 + e] = __builtin_bit_cast(f16x2, ww[e >> 1])[e & 1];
       }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        uint32_t whi = 0, wlo = 0;
+        // four codes of this word: q_f = rint(q~ / sigma), split into hi = (q_f + 128) >> 8
+        // and lo = q_f - 256 hi as int16 pairs, whose low bytes form the two operand words
+        float qf[4];
 #pragma unroll
         for (int b = 0; b < 4; b++) {
           const int c = kperm<BITS>(j, b);
-          const int qf = (int)__builtin_rintf(qv[16 * kk + c] * inv);
-          const int hi = (qf + 128) >> 8;
-          const int lo = qf - (hi << 8);
-          zs = fmaf((float)qf, zt[c], zs);
-          whi |= (uint32_t)(hi & 0xFF) << (8 * b);
-          wlo |= (uint32_t)(lo & 0xFF) << (8 * b);
+          qf[b] = __builtin_rintf(qv[16 * kk + c] * inv);
+          zs = fmaf(qf[b], (float)zt[c], zs);
         }
-        qhi[kk][j] = (int)whi;
-        qlo[kk][j] = (int)wlo;
+        const s16x2 p0 = __builtin_amdgcn_cvt_pk_i16((int)qf[0], (int)qf[1]);
+        const s16x2 p1 = __builtin_amdgcn_cvt_pk_i16((int)qf[2], (int)qf[3]);
+        const s16x2 h0 = (p0 + (short)128) >> (short)8, h1 = (p1 + (short)128) >> (short)8;
+        const s16x2 l0 = p0 - (h0 << (short)8), l1 = p1 - (h1 << (short)8);
+        qhi[kk][j] = (int)__builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, h1), __builtin_bit_cast(uint32_t, h0), 0x06040200u);
+        qlo[kk][j] = (int)__builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, l1), __builtin_bit_cast(uint32_t, l0), 0x06040200u);
       }
     }
     zs += xor32(zs);
@@ -1046,6 +1063,51 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   return KVQ_OK;
 }
 
+// q' = H q / sqrt(D) in fp32 for every query (keys quantized per channel re-quantize the
+// rotated query at every key group; rotating once per call spares each group the
+// transform). Two lanes per query, half a row each, in the order the attention kernel's
+// own rotation uses: butterflies inside the lane, then across the pair.
+template <int D>
+__global__ __launch_bounds__(256) void jb_rotate_q_kernel(const uint16_t* __restrict__ q, size_t rows,
+                                                          float* __restrict__ qrot) {
+  constexpr int HALF = D / 2;
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = t >> 1;
+  const int h = (int)(t & 1);
+  const bool ok = row < rows;
+  const uint4* src = reinterpret_cast<const uint4*>(q + (ok ? row : 0) * D + HALF * h);
+  float qv[HALF];
+#pragma unroll
+  for (int u = 0; u < HALF / 8; u++) {
+    const uint4 w = src[u];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      qv[8 * u + 2 * e] = __uint_as_float(ww[e] << 16);
+      qv[8 * u + 2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int hh = 1; hh < HALF; hh <<= 1)
+#pragma unroll
+    for (int i = 0; i < HALF; i++)
+      if ((i & hh) == 0) {
+        const float a = qv[i], b = qv[i + hh];
+        qv[i] = a + b;
+        qv[i + hh] = a - b;
+      }
+  const float c = rsqrtf((float)D);
+#pragma unroll
+  for (int i = 0; i < HALF; i++) {
+    const float pv = __shfl_xor(qv[i], 1);
+    qv[i] = (h ? (pv - qv[i]) : (qv[i] + pv)) * c;
+  }
+  if (!ok) return;
+  float4* dst = reinterpret_cast<float4*>(qrot + row * D + HALF * h);
+#pragma unroll
+  for (int u = 0; u < HALF / 4; u++) dst[u] = make_float4(qv[4 * u], qv[4 * u + 1], qv[4 * u + 2], qv[4 * u + 3]);
+}
+
 // Combines the partial records of the n_split shares of each query: with M the largest
 // reference max, weights w = 2^(m - M); O = sum w acc / sum w (l_S + l_R), and the
 // masses from the weighted sums. One thread per (query, 4 output channels); G threads
@@ -1090,6 +1152,7 @@ __global__ __launch_bounds__(256) void jb_combine_kernel(const float* __restrict
 struct AttnPlan {
   int n_qblk, n_split;
   size_t part_bytes;  // workspace the split needs (0 for n_split == 1)
+  size_t qrot_bytes;  // workspace of the rotated queries (per-channel rotated keys), else 0
 };
 
 // Splits each query block's tile sequence over n_split workgroups when that shortens the
@@ -1101,6 +1164,9 @@ AttnPlan plan_attn(const jb_attn_args* a) {
   pl.n_qblk = (a->n_q + kBM - 1) / kBM;
   pl.n_split = 1;
   pl.part_bytes = 0;
+  pl.qrot_bytes = (a->k_fmt.granularity == KVQ_PER_CHANNEL && a->k_fmt.hadamard && a->n_chunks > 0)
+                      ? (size_t)a->B * a->H * a->n_q * (size_t)a->d * sizeof(float)
+                      : 0;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 1) {
@@ -1149,8 +1215,15 @@ int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   p.k_had = a->k_fmt.hadamard;
   p.v_had = a->v_fmt.hadamard;
   p.k_group = PERCH ? a->k_fmt.group : 0;
+  // workspace: [rotated queries][split partials], each 16-byte aligned
+  char* ws = static_cast<char*>(a->workspace);
+  p.qrot = pl.qrot_bytes ? reinterpret_cast<const float*>(ws) : nullptr;
   p.n_split = pl.n_split;
-  p.part = pl.n_split > 1 ? static_cast<float*>(a->workspace) : nullptr;
+  p.part = pl.n_split > 1 ? reinterpret_cast<float*>(ws + pl.qrot_bytes) : nullptr;
+  if (pl.qrot_bytes) {
+    const size_t rows = (size_t)a->B * a->H * a->n_q;
+    jb_rotate_q_kernel<D><<<(unsigned)((2 * rows + 255) / 256), 256, 0, st>>>(a->q, rows, reinterpret_cast<float*>(ws));
+  }
   p.o = MASS_ONLY ? nullptr : a->o;
   p.mass_s = a->mass_s;
   p.mass_r = a->mass_r;
@@ -1170,9 +1243,15 @@ int dispatch(const jb_attn_args* a, void* stream) {
   const int st = validate_attn(a, MASS_ONLY);
   if (st) return st;
   AttnPlan pl = plan_attn(a);
-  // without a workspace large enough for the partials the call runs unsplit
-  if (pl.n_split > 1 && (!a->workspace || a->workspace_bytes < pl.part_bytes)) pl.n_split = 1;
-  if (pl.n_split > 1 && !aligned16(a->workspace)) return KVQ_ERR_ALIGN;
+  // the workspace serves the rotated queries first, then the split partials; what does
+  // not fit is done without (in-kernel rotation, an unsplit grid)
+  const size_t have = a->workspace ? a->workspace_bytes : 0;
+  if (pl.qrot_bytes && have < pl.qrot_bytes) pl.qrot_bytes = 0;
+  if (pl.n_split > 1 && have < pl.qrot_bytes + pl.part_bytes) {
+    pl.n_split = 1;
+    pl.part_bytes = 0;
+  }
+  if ((pl.qrot_bytes || pl.n_split > 1) && !aligned16(a->workspace)) return KVQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool perch = a->k_fmt.granularity == KVQ_PER_CHANNEL;
   if (a->d == 128) {
@@ -1194,5 +1273,6 @@ extern "C" int jb_attn_mass(const jb_attn_args* a, void* stream) { return kvq::d
 
 extern "C" size_t jb_attn_workspace_bytes(const jb_attn_args* a) {
   if (kvq::validate_attn(a, false) != KVQ_OK && kvq::validate_attn(a, true) != KVQ_OK) return 0;
-  return kvq::plan_attn(a).part_bytes;
+  const kvq::AttnPlan pl = kvq::plan_attn(a);
+  return pl.qrot_bytes + pl.part_bytes;
 }

@@ -171,6 +171,23 @@ def test_per_channel_keys_all_rows(shape, bits, correction):
     assert_mass_close(PS, PR, PSr, PRr, f"perch {shape} b{bits} c{correction}")
 
 
+@pytest.mark.parametrize("shape", PERCH[:2], ids=lambda s: "x".join(str(v) for v in s.values()))
+def test_per_channel_keys_without_workspace(shape):
+    """Per-channel keys with no workspace: the kernel rotates the query itself at every key
+    group (with one, a pre-pass rotates every query once and the call may also split)."""
+    w = synth.Workload("perch", **shape, bits=2, k_dist="t3", k_granularity="channel", seed=11)
+    print(f"attn per-channel {shape} without workspace", flush=True)
+    x = synth.draw_all(w)
+    a = run_gpu(x, w, split=False)
+    assert run_gpu.last_workspace_bytes == 0
+    b = run_gpu(x, w, split=True)
+    assert run_gpu.last_workspace_bytes > 0
+    Or, PSr, PRr = run_oracle(x, w)
+    for label, r in (("no workspace", a), ("workspace", b)):
+        assert_attention_close(r[0], Or, f"perch {label}")
+        assert_mass_close(r[1], r[2], PSr, PRr, f"perch {label}")
+
+
 def _bf16_bits(a):
     u = np.asarray(a, np.float32).view(np.uint32)
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)

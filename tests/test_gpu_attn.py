@@ -8,6 +8,8 @@ masses within 1e-3 and P_S + P_R = 1 within 1e-6.
 Small shapes are checked on every row; the full workloads run the full call on the
 GPU and check sampled rows of sampled heads (the oracle computes those rows exactly).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -25,9 +27,10 @@ def _kvq():
 
 
 def run_gpu(x, w, *, k_had=True, v_had=True, bits=None, correction=1, masses=True, mass_only=False, scale=0.0,
-            split=True):
+            split=True, ws_bytes=None):
     """Pack the window and run one call; returns numpy (O, P_S, P_R). split=False runs
-    without a workspace (no split-window partials)."""
+    without a workspace; ws_bytes gives the call a workspace of that many bytes instead
+    of the size the library asks for."""
     kvq = _kvq()
     kf, vf = lib_formats(w, k_had, v_had, bits)
     q, kr, vr = dev(x["q"]), dev(x["k_cur"]), dev(x["v_cur"])
@@ -43,7 +46,12 @@ def run_gpu(x, w, *, k_had=True, v_had=True, bits=None, correction=1, masses=Tru
     args = kvq.make_args(q, kr if x["k_cur"].shape[2] else None, vr if x["k_cur"].shape[2] else None, kwin, vwin,
                          w.chunk_len, w.n_chunks, kf, vf, o=o, mass_s=ms, mass_r=mr, correction=correction,
                          softmax_scale=scale)
-    ws = kvq.attach_workspace(args) if split else None
+    run_gpu.wanted_workspace_bytes = kvq.jb_attn_workspace_bytes(args)
+    if ws_bytes is not None:
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        args.workspace, args.workspace_bytes = ctypes.c_void_p(ws.data_ptr()), ws_bytes
+    else:
+        ws = kvq.attach_workspace(args) if split else None
     run_gpu.last_workspace_bytes = args.workspace_bytes
     if mass_only:
         kvq.jb_attn_mass(args)
@@ -182,8 +190,12 @@ def test_per_channel_keys_without_workspace(shape):
     assert run_gpu.last_workspace_bytes == 0
     b = run_gpu(x, w, split=True)
     assert run_gpu.last_workspace_bytes > 0
+    # room for the rotated queries only: rotation pre-pass, no split
+    qrot_bytes = w.B * w.H * w.n_q * w.d * 4
+    assert run_gpu.wanted_workspace_bytes > qrot_bytes, "expected a split plan as well"
+    c = run_gpu(x, w, ws_bytes=qrot_bytes)
     Or, PSr, PRr = run_oracle(x, w)
-    for label, r in (("no workspace", a), ("workspace", b)):
+    for label, r in (("no workspace", a), ("workspace", b), ("rotation only", c)):
         assert_attention_close(r[0], Or, f"perch {label}")
         assert_mass_close(r[1], r[2], PSr, PRr, f"perch {label}")
 

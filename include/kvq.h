@@ -145,7 +145,9 @@ typedef struct {
  * fp16 (relative to a per-query reference max that is raised whenever a numerator could
  * leave the fp16 range), values fp16((code - z) Delta); sums and outputs fp32.
  * Preconditions on the data (not checked): key steps Delta < 2048 and |Delta z| < 65504
- * (per token), scaled logits |s q.k| and the correction below 2^15 nats.
+ * (per token); value zero points -2032 <= z <= 1024 (code - z is then formed exactly in
+ * fp16) and |(code - z) Delta| < 65504; scaled logits |s q.k| and the correction below
+ * 2^15 nats.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (also when one head's cached codes exceed 2^31 - 1
  * bytes), KVQ_ERR_UNSUPPORTED (mixed bits, value per-channel, wrong roles, group not
  * 64/128), KVQ_ERR_ALIGN (also a misaligned workspace that a split would use), KVQ_ERR_HIP. */

@@ -205,6 +205,29 @@ def _bf16_bits(a):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
+@pytest.mark.parametrize("had", [True, False])
+def test_degenerate_cache_tokens(had):
+    """Cached tokens whose quantization is degenerate: all-zero keys and values (step 0,
+    codes 0, no correction) and tokens far from zero (zero points far outside the code
+    range), rotated or not."""
+    w = synth.Workload("degen", B=1, H=2, d=128, n_q=96, chunk_len=100, n_chunks=2, bits=2, seed=5)
+    x = dict(synth.draw_all(w))
+    rng = np.random.default_rng(9)
+    kc, vc = x["k_cache"].copy(), x["v_cache"].copy()
+    kc[0, 0, 5] = 0
+    vc[0, 0, 5] = 0
+    vc[0, 1, 150] = 0
+    kc[0, 1, 30] = _bf16_bits(5.0 + rng.random(w.d))     # keys in [5, 6): z = rint(-min/step) far below 0
+    vc[0, 1, 31] = _bf16_bits(-40.0 + rng.random(w.d))   # values in [-40, -39): z far above the codes
+    kc[0, 0, 180] = _bf16_bits(np.full(w.d, 0.75))       # one value in every channel
+    x["k_cache"], x["v_cache"] = kc, vc
+    print(f"attn degenerate tokens hadamard={had}", flush=True)
+    O, PS, PR = run_gpu(x, w, k_had=had, v_had=had)
+    Or, PSr, PRr = run_oracle(x, w, k_had=had, v_had=had)
+    assert_attention_close(O, Or, f"degenerate had={had}")
+    assert_mass_close(PS, PR, PSr, PRr, f"degenerate had={had}")
+
+
 @pytest.mark.parametrize("gain", [3.0, 6.0, 12.0])
 def test_late_dominant_key(gain):
     """A key near the window's end scores tens of nats above the first keys, past what

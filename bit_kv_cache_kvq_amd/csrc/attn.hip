@@ -224,6 +224,9 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   const int qb = qbs / p.n_split, sp = qbs % p.n_split;  // query block, share of the tiles
   const int qi = qb * kBM + wave * 32 + col;  // this lane's query
   const bool q_ok = qi < p.n_q;
+  // A wave whose 32 queries all lie past n_q (in the ragged last query block) stages tiles
+  // and takes the barriers with the others but computes nothing.
+  const bool computes = __builtin_amdgcn_readfirstlane(__ballot(q_ok) != 0ull ? 1 : 0) != 0;
   const float scale_l2 = p.s * kLog2e;  // softmax scale in log2 units
 
   // ---------------- query operands ----------------
@@ -914,27 +917,31 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     const bool stage_k = T + 2 < n_t, stage_v = T + 1 < n_t;
     if (stage_k) load_k(U + 2, k_c);
     if (stage_v) load_v(U + 1, k_c);
-    if constexpr (PERCH && decltype(k_c)::value == kCached) {
-      if (T == 0 || (U % tiles_per_chunk) % k_tpg == 0) refresh_group(U);
+    if (computes) {
+      if constexpr (PERCH && decltype(k_c)::value == kCached) {
+        if (T == 0 || (U % tiles_per_chunk) % k_tpg == 0) refresh_group(U);
+      }
+      // operand reads are issued one phase ahead of their MFMAs (the sched barriers keep
+      // the compiler from sinking them): values under the softmax, keys under the PV
+      read_k(slot0, 0, k_c);
+      qk(set0, k_c);
+      read_v(slot0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(slot0, 0, set0, k_c, first_c);
+      read_k(slot0, 1, k_c);
+      __builtin_amdgcn_sched_barrier(0);
+      pv();
+      qk(set0, k_c);
+      read_v(slot0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // the key staging (VALU and LDS writes) runs in the shadow of block 1's QK^T MFMAs
+      if (stage_k) store_k(U + 2, slot2, k_c);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(slot0, 1, set0, k_c, no);
+      pv();
+    } else if (stage_k) {
+      store_k(U + 2, slot2, k_c);
     }
-    // operand reads are issued one phase ahead of their MFMAs (the sched barriers keep
-    // the compiler from sinking them): values under the softmax, keys under the PV
-    read_k(slot0, 0, k_c);
-    qk(set0, k_c);
-    read_v(slot0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    softmax(slot0, 0, set0, k_c, first_c);
-    read_k(slot0, 1, k_c);
-    __builtin_amdgcn_sched_barrier(0);
-    pv();
-    qk(set0, k_c);
-    read_v(slot0, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    // the key staging (VALU and LDS writes) runs in the shadow of block 1's QK^T MFMAs
-    if (stage_k) store_k(U + 2, slot2, k_c);
-    __builtin_amdgcn_sched_barrier(0);
-    softmax(slot0, 1, set0, k_c, no);
-    pv();
     if (stage_v) store_v(U + 1, slot1, k_c);
     __syncthreads();
   };
@@ -972,7 +979,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   if (c_end > c_beg) {
     run(c_beg, c_end - c_beg, Kind<kCached>());
     if constexpr (!MASS_ONLY) {
-      if (p.v_had) unrotate();
+      if (p.v_had && computes) unrotate();
     }
   }
   if (r_end > r_beg) {

@@ -394,12 +394,11 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   const int k_tpg = PERCH ? p.k_group / kBN : 1;                       // tiles per key group
   const int k_gpc = PERCH ? (p.chunk_len + p.k_group - 1) / p.k_group : 1;  // groups per chunk
   float a_ch = 0.f;
-  auto refresh_group = [&](int U) KVQ_INLINE {
-    const int ci = U / tiles_per_chunk, t = U % tiles_per_chunk;
-    const size_t gi = (size_t)ci * k_gpc + t / k_tpg;
-    const size_t prow = ((size_t)bh * p.n_chunks * k_gpc + gi) * D + HALF * h;
-    const uint4* drow = reinterpret_cast<const uint4*>(p.k_scale + prow);
-    const uint4* zrow = reinterpret_cast<const uint4*>(p.k_zero + prow);
+  // The group's step and zero-point rows come from the tile's parameter slot (staged with
+  // the tile's keys): D fp16 steps, then D fp16 zero points.
+  auto refresh_group = [&](int slot) KVQ_INLINE {
+    const uint4* drow = reinterpret_cast<const uint4*>(&sm.prm[slot].dka[0][0]) + HALF * h / 8;
+    const uint4* zrow = drow + D / 8;
     float qv[HALF];
     if (p.qrot) {  // rotated once for the whole call by jb_rotate_q_kernel
       const float4* src = reinterpret_cast<const float4*>(p.qrot + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h);
@@ -478,6 +477,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   uint4 kpre[RIPT];          // keys (code units, or current rows)
   uint4 vpre[2 * VRPT];      // values (code groups, or current row pairs)
   uint32_t pk_dk = 0, pk_zk = 0;                 // key step / zero point of key tid & 63
+  uint4 gpre = make_uint4(0, 0, 0, 0);           // per-channel keys: 16 bytes of the group rows
   uint32_t pz0 = 0, pz1 = 0, pd0 = 0, pd1 = 0;   // value zero points / steps of a token pair
 
   auto load_k = [&](int U, auto k_c) KVQ_INLINE {
@@ -499,6 +499,13 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         const uint32_t j = (uint32_t)(tid & (kBN - 1));
         pk_dk = __builtin_amdgcn_raw_buffer_load_b16(rs_ks, j * 2u, tok0 * 2u, 0);
         pk_zk = __builtin_amdgcn_raw_buffer_load_b16(rs_kz, j * 2u, tok0 * 2u, 0);
+      } else if (tid < D / 4) {
+        // per-channel keys: the step row (lanes 0 .. D/8-1) and zero-point row of the
+        // tile's key group, 16 bytes per lane
+        const int ci = U / tiles_per_chunk, tt = U % tiles_per_chunk;
+        const size_t row = ((size_t)bh * p.n_chunks * k_gpc + (size_t)ci * k_gpc + tt / k_tpg) * D;
+        const uint16_t* src = tid < D / 8 ? p.k_scale : p.k_zero;
+        gpre = reinterpret_cast<const uint4*>(src + row)[tid % (D / 8)];
       }
       if constexpr (!MASS_ONLY) {
         const uint32_t j = (uint32_t)(16 * ((tid >> 3) & 3) + (tid & 7));
@@ -538,6 +545,9 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         *reinterpret_cast<uint4*>(&ks.c[tok][16 * ui]) = lo;
       }
       // Delta_j A of each wave's stream; 0 for padding keys (their logit is set by the mask)
+      if constexpr (PERCH) {
+        if (tid < D / 4) reinterpret_cast<uint4*>(&ps.dka[0][0])[tid] = gpre;
+      }
       if constexpr (!PERCH) {
         const int key = tid & (kBN - 1);
         const int r = 32 * (key >> 5) + key_mrow(key & 31);
@@ -919,7 +929,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     if (stage_v) load_v(U + 1, k_c);
     if (computes) {
       if constexpr (PERCH && decltype(k_c)::value == kCached) {
-        if (T == 0 || (U % tiles_per_chunk) % k_tpg == 0) refresh_group(U);
+        if (T == 0 || (U % tiles_per_chunk) % k_tpg == 0) refresh_group(slot0);
       }
       // operand reads are issued one phase ahead of their MFMAs (the sched barriers keep
       // the compiler from sinking them): values under the softmax, keys under the PV

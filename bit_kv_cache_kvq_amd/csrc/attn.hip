@@ -815,15 +815,15 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   };
   // fp16 P pairs with p = exp2(x - off) into pb; returns this lane's fp16 sum.
   auto pairs = [&](const float* x, float off) KVQ_INLINE {
-    float lsum = 0.f;
+    float ls2[2] = {0.f, 0.f};  // two dependency chains of four dot2 each
     const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
     for (int v2 = 0; v2 < 8; v2++) {
       const uint32_t pr = pack_f16x2(exp2_(x[2 * v2] - off), exp2_(x[2 * v2 + 1] - off));
       pb[v2 >> 2][v2 & 3] = pr;
-      lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pr), ones, lsum, false);
+      ls2[v2 & 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pr), ones, ls2[v2 & 1], false);
     }
-    return lsum;
+    return ls2[0] + ls2[1];
   };
   // Softmax numerators of block mb of tile U (scores in SET). The reference m starts at
   // the maximum of the stream's first block plus a headroom of 2^2 (FIRST) and is raised

@@ -30,6 +30,7 @@ PEAK_MFMA_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "jb_attn TFLOP/s + cache GB/s (% roofline), INT2 corrected, 40H d128 chunk 4680"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "jb_attn_c40_counters.md")
+CORR_NAMES = {0: "none", 1: "taylor", 2: "exact"}
 KERNEL_SOURCE = os.path.join(ROOT, "bit_kv_cache_kvq_amd", "csrc", "attn.hip")
 
 
@@ -51,7 +52,7 @@ def traffic_from_profile():
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(w, x, heads, kf_o, vf_o):
+def cpu_baseline(w, x, heads, kf_o, vf_o, correction="taylor"):
     """Time the oracle (as it stands) on `heads`: pack of the current chunk + attention."""
     import numpy as np
     import oracle
@@ -68,7 +69,7 @@ def cpu_baseline(w, x, heads, kf_o, vf_o):
     pack_window(xs["k_cur"], w.n_r, kf_o)
     pack_window(xs["v_cur"], w.n_r, vf_o)
     O, PS, PR, _ = oracle.reference_call(xs["q"], xs["k_cache"], xs["v_cache"], xs["k_cur"], xs["v_cur"],
-                                         chunk_len=w.chunk_len, k_fmt=kf_o, v_fmt=vf_o, correction="taylor",
+                                         chunk_len=w.chunk_len, k_fmt=kf_o, v_fmt=vf_o, correction=correction,
                                          cache=cache)
     dt = time.perf_counter() - t0
     flops = 4.0 * w.n_q * (w.n_c + w.n_r) * w.d * len(heads)
@@ -85,7 +86,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c40")
     ap.add_argument("--bits", type=int, default=None)
-    ap.add_argument("--correction", type=int, default=1)
+    ap.add_argument("--correction", type=int, default=1, choices=sorted(CORR_NAMES),
+                    help="0 none, 1 second-order Taylor (the headline), 2 exact")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle timing sample (0: skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="only run a device copy of this many MiB (HBM counter calibration) and exit")
@@ -188,7 +190,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} d={w.d}, current chunk {w.n_q} tokens, window "
                                f"{w.n_chunks}x{w.chunk_len} cached tokens, INT{w.bits} per-{w.k_granularity} K, "
-                               f"per-token V, Hadamard, correction={'taylor' if args.correction else 'none'}",
+                               f"per-token V, Hadamard, correction={CORR_NAMES[args.correction]}",
                    "B": w.B, "H": w.H, "d": w.d, "n_q": w.n_q, "n_c": w.n_c, "bits": w.bits,
                    "parallelism": "none (1 GPU)", "split_workspace_bytes": a.workspace_bytes},
         "attn_ms": round(attn_ms, 4),
@@ -207,7 +209,7 @@ def main():
             [(b, h) for b in range(w.B) for h in range(w.H)][: args.cpu_heads]
         kf_o = Format(w.bits, w.k_granularity, w.group, True, "key")
         vf_o = Format(w.bits, "token", w.group, True, "value")
-        base, (O, PS, PR) = cpu_baseline(w, x, heads, kf_o, vf_o)
+        base, (O, PS, PR) = cpu_baseline(w, x, heads, kf_o, vf_o, CORR_NAMES[args.correction])
         og = np.stack([o[b, h].cpu().numpy() for (b, h) in heads])[None]
         rms = np.sqrt((O ** 2).mean())
         err = np.abs(og - O)

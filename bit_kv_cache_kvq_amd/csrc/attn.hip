@@ -135,6 +135,16 @@ __device__ inline void split16(float x, _Float16& hi, _Float16& lo) {
 
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32); }
 
+// log(sinh(x) / x), the logarithm of E[e^(2 x u)] for u uniform on [-1/2, 1/2]: its
+// power series through x^10 (coefficients 2^2n B_2n / (2n (2n)!), omitted terms below
+// 1.7e-7 for |x| < 1), else |x| - log(2|x|) + log(1 - e^(-2|x|)).
+__device__ inline float log_sinhc(float x) {
+  const float a = fabsf(x), u = a * a;
+  if (a < 1.f)
+    return u * (1.f / 6 - u * (1.f / 180 - u * (1.f / 2835 - u * (1.f / 37800 - u * (1.f / 467775)))));
+  return a - __logf(2.f * a) + __logf(1.f - __expf(-2.f * a));
+}
+
 // Raw buffer descriptor over [base, base + bytes): loads take a per-lane 32-bit offset
 // and a wave-uniform offset (scalar register), so no 64-bit per-lane addresses are kept.
 // Loads past the end return 0.
@@ -167,6 +177,8 @@ struct Smem {
   struct PSlot {
     float dka[kNS][kBN];  // Delta_j A of each stream (cached; 0 for padding), M-row order
     uint4 kb[kBN][2];     // bias operand rows (16 fp16), M-row order
+    float d2[kBN];        // exact correction, per-token keys: Delta_j^2 and Delta_j^4, M-row order
+    float d4[kBN];
   };
   struct ZSlot {
     uint32_t zv[kBN / 2];   // (-1024 - z^V) fp16 pairs, token pair (j, j+8) order
@@ -185,7 +197,7 @@ enum : int { kNone = 0, kCached = 1, kCurrent = 2 };
 template <int K>
 using Kind = std::integral_constant<int, K>;
 
-template <int D, int BITS, bool MASS_ONLY, bool PERCH>
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
 __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   using SM = Smem<D>;
   constexpr int HALF = D / 2;
@@ -268,6 +280,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   };
   // -m, plus the key group's constant c_grp (per-channel keys), into query slots 8, 9.
   float c_grp = 0.f;
+  float ex2 = 0.f, ex3 = 0.f, ex4 = 0.f;  // exact correction, per-token keys (log2 units)
   auto write_mslot = [&]() KVQ_INLINE {
     _Float16 mh = (_Float16)0.f, ml = (_Float16)0.f;
     split16(c_grp - (m_run == -INFINITY ? 0.f : m_run), mh, ml);
@@ -308,6 +321,24 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       }
     qs += __shfl_xor(qs, 32);
     const float G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
+    if constexpr (EXACT && !PERCH) {
+      // b(Delta) = sum_c log_sinhc(s q'_c Delta / 2) = sum_n c_n M_n Delta^2n with
+      // M_n = sum_c (s q'_c / 2)^2n: the n = 1 term is G's, n = 2..4 enter the logits
+      float m2 = 0.f, m3 = 0.f, m4 = 0.f;
+#pragma unroll
+      for (int i = 0; i < HALF; i++) {
+        const float y = 0.5f * p.s * qv[i], u = y * y, u2 = u * u;
+        m2 += u2;
+        m3 = fmaf(u2, u, m3);
+        m4 = fmaf(u2, u2, m4);
+      }
+      m2 += xor32(m2);
+      m3 += xor32(m3);
+      m4 += xor32(m4);
+      ex2 = m2 * (1.f / 180.f) * kLog2e;
+      ex3 = m3 * (1.f / 2835.f) * kLog2e;
+      ex4 = m4 * (1.f / 37800.f) * kLog2e;
+    }
     // query-side factors of the bias MFMA (key side in the tile parameters):
     //   (Delta_j z_j) * w + (Delta_j^2 / 64) * g - m - 65504 * mask_j
     const float w = -A * (float)qs;
@@ -429,6 +460,12 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       }
     }
     ss += xor32(ss);
+    float bx = 0.f;  // exact correction: sum_c log_sinhc(s q~_c / 2)
+    if constexpr (EXACT) {
+#pragma unroll
+      for (int i = 0; i < HALF; i++) bx += log_sinhc(0.5f * p.s * qv[i]);
+      bx += xor32(bx);
+    }
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));  // stream-wide max
     const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
@@ -464,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       }
     }
     zs += xor32(zs);
-    const float G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
+    const float G = EXACT ? bx * kLog2e : p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
     c_grp = -a_ch * zs - G;
     write_mslot();
   };
@@ -553,6 +590,10 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         const int r = 32 * (key >> 5) + key_mrow(key & 31);
         const float dk = key < nv ? half_bits_to_f32(pk_dk) : 0.f;
         ps.dka[wave][r] = dk * a_st;
+        if (EXACT && !PERCH && wave == 3) {
+          ps.d2[r] = dk * dk;
+          ps.d4[r] = (dk * dk) * (dk * dk);
+        }
       }
       if (PERCH && wave == 0) {
         // per-channel keys: the group terms ride on the query side (slots 8, 9)
@@ -807,6 +848,19 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
           const int v = 4 * v4 + b;
           x[v] = fmaf(d[b], (float)sqh[SET][v], cb[SET][v]);
         }
+        if constexpr (EXACT && !PERCH) {
+          // the exact correction's terms past the second order: -b gains
+          // Delta^4 (c2 M2 - Delta^2 (c3 M3 - Delta^2 c4 M4))
+          const float4 e2v = *reinterpret_cast<const float4*>(&sm.prm[slot].d2[32 * mb + 8 * v4 + 4 * h]);
+          const float4 e4v = *reinterpret_cast<const float4*>(&sm.prm[slot].d4[32 * mb + 8 * v4 + 4 * h]);
+          const float dd2[4] = {e2v.x, e2v.y, e2v.z, e2v.w}, dd4[4] = {e4v.x, e4v.y, e4v.z, e4v.w};
+#pragma unroll
+          for (int b = 0; b < 4; b++) {
+            const int v = 4 * v4 + b;
+            const float t = fmaf(-dd2[b], fmaf(-dd2[b], ex4, ex3), ex2);
+            x[v] = fmaf(dd4[b], t, x[v]);
+          }
+        }
       }
     } else {
 #pragma unroll
@@ -1049,7 +1103,8 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   if (kf.granularity != KVQ_PER_TOKEN && kf.granularity != KVQ_PER_CHANNEL) return KVQ_ERR_UNSUPPORTED;
   if (kf.granularity == KVQ_PER_CHANNEL && kf.group != 64 && kf.group != 128) return KVQ_ERR_UNSUPPORTED;
   if ((kf.hadamard | vf.hadamard) & ~1) return KVQ_ERR_UNSUPPORTED;
-  if (a->correction != JB_CORR_NONE && a->correction != JB_CORR_TAYLOR) return KVQ_ERR_UNSUPPORTED;
+  if (a->correction != JB_CORR_NONE && a->correction != JB_CORR_TAYLOR && a->correction != JB_CORR_EXACT)
+    return KVQ_ERR_UNSUPPORTED;
   if (a->d != 64 && a->d != 128) return KVQ_ERR_SHAPE;
   if (a->B < 1 || a->H < 1 || a->n_q < 1 || a->n_r < 0 || a->chunk_len < 1 || a->n_chunks < 0)
     return KVQ_ERR_SHAPE;
@@ -1207,7 +1262,7 @@ AttnPlan plan_attn(const jb_attn_args* a) {
   return pl;
 }
 
-template <int D, int BITS, bool MASS_ONLY, bool PERCH>
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT = false>
 int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   Params p;
   p.B = a->B;
@@ -1245,7 +1300,7 @@ int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   p.mass_s = a->mass_s;
   p.mass_r = a->mass_r;
   const unsigned grid = (unsigned)(pl.n_qblk * a->B * a->H * pl.n_split);
-  jb_attn_kernel<D, BITS, MASS_ONLY, PERCH><<<grid, kThreads, 0, st>>>(p);
+  jb_attn_kernel<D, BITS, MASS_ONLY, PERCH, EXACT><<<grid, kThreads, 0, st>>>(p);
   if (pl.n_split > 1) {
     const size_t rows = (size_t)a->B * a->H * a->n_q;
     constexpr int G = MASS_ONLY ? 1 : D / 4;
@@ -1271,6 +1326,18 @@ int dispatch(const jb_attn_args* a, void* stream) {
   if ((pl.qrot_bytes || pl.n_split > 1) && !aligned16(a->workspace)) return KVQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool perch = a->k_fmt.granularity == KVQ_PER_CHANNEL;
+  if (a->correction == JB_CORR_EXACT && a->n_chunks > 0) {
+    if (a->d == 128) {
+      if (a->k_fmt.bits == 2)
+        return perch ? launch_attn<128, 2, MASS_ONLY, true, true>(a, pl, s)
+                     : launch_attn<128, 2, MASS_ONLY, false, true>(a, pl, s);
+      return perch ? launch_attn<128, 4, MASS_ONLY, true, true>(a, pl, s)
+                   : launch_attn<128, 4, MASS_ONLY, false, true>(a, pl, s);
+    }
+    if (a->k_fmt.bits == 2)
+      return perch ? launch_attn<64, 2, MASS_ONLY, true, true>(a, pl, s) : launch_attn<64, 2, MASS_ONLY, false, true>(a, pl, s);
+    return perch ? launch_attn<64, 4, MASS_ONLY, true, true>(a, pl, s) : launch_attn<64, 4, MASS_ONLY, false, true>(a, pl, s);
+  }
   if (a->d == 128) {
     if (a->k_fmt.bits == 2)
       return perch ? launch_attn<128, 2, MASS_ONLY, true>(a, pl, s) : launch_attn<128, 2, MASS_ONLY, false>(a, pl, s);

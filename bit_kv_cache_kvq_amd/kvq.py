@@ -18,7 +18,7 @@ library_path = os.environ.get("KVQ_LIBRARY") or os.path.join(_HERE, "libkvq.so")
 
 KVQ_PER_TOKEN, KVQ_PER_CHANNEL = 0, 1
 KVQ_ROLE_KEY, KVQ_ROLE_VALUE = 0, 1
-JB_CORR_NONE, JB_CORR_TAYLOR = 0, 1
+JB_CORR_NONE, JB_CORR_TAYLOR, JB_CORR_EXACT = 0, 1, 2
 
 EXPORTS = ("kvq_chunk_pad", "kvq_window_elems", "kvq_pack", "jb_attn_fwd", "jb_attn_mass",
            "jb_attn_workspace_bytes", "kvq_status_str")

@@ -48,7 +48,7 @@ enum {
 
 enum { KVQ_PER_TOKEN = 0, KVQ_PER_CHANNEL = 1 };
 enum { KVQ_ROLE_KEY = 0, KVQ_ROLE_VALUE = 1 };
-enum { JB_CORR_NONE = 0, JB_CORR_TAYLOR = 1 };
+enum { JB_CORR_NONE = 0, JB_CORR_TAYLOR = 1, JB_CORR_EXACT = 2 };
 
 /* Storage format of one cached tensor.
  *
@@ -113,7 +113,14 @@ int kvq_pack(const uint16_t* x, int32_t B, int32_t H, int32_t n, int32_t d, cons
  * where q' = H q if the keys were rotated (else q), Delta_jc is the key's step size
  * (per token: the same for every c, giving b_ij = s^2 |q_i|^2 Delta_j^2 / 24), and
  * b is the second-order Taylor form of the expected inflation of e^l under uniform
- * rounding noise on the cached keys. b_ij = 0 when correction == JB_CORR_NONE. */
+ * rounding noise on the cached keys. b_ij = 0 when correction == JB_CORR_NONE.
+ * JB_CORR_EXACT replaces b by the logarithm of that inflation itself (Fig. 3 caption's
+ * model, an ablation of the second-order form):
+ *   b_ij = sum_c log(sinh(x) / x),  x = s q'_ic Delta_jc / 2.
+ * Per-channel keys evaluate it once per query and key group (relative error of each
+ * channel's term below 1e-6). Per-token keys evaluate its power series in Delta_j through
+ * Delta_j^8 (the omitted terms are below (max_c x)^8 sum_c x^2 / 467775 nats: 2e-6 per
+ * channel at x = 1; the series does not converge past x = pi). */
 typedef struct {
   int32_t B, H, d;            /* d in {64, 128}; the same H for queries and keys */
   int32_t n_q;                /* current-chunk queries, >= 1 */
@@ -131,7 +138,7 @@ typedef struct {
   const uint16_t* v_zero;
   kvq_format k_fmt, v_fmt;    /* same bits; k: KEY per token or per channel; v: VALUE per token */
   float softmax_scale;        /* s; 0 selects 1/sqrt(d) */
-  int32_t correction;         /* JB_CORR_NONE or JB_CORR_TAYLOR */
+  int32_t correction;         /* JB_CORR_NONE, JB_CORR_TAYLOR or JB_CORR_EXACT */
   float* o;                   /* fp32 [B, H, n_q, d]: required by fwd, ignored by mass */
   float* mass_s;              /* fp32 [B, H, n_q]: optional in fwd (NULL), required in mass */
   float* mass_r;              /* fp32 [B, H, n_q]: as mass_s */

@@ -101,6 +101,8 @@ def test_attn_validation_without_launch(kvq):
     assert fwd(args(n_q=0)) == -2
     assert fwd(args(n_chunks=0, n_r=0)) == -2
     assert fwd(args(correction=7)) == -3
+    assert fwd(args(correction=3)) == -3
+    assert fwd(args(correction=2, o=None)) == -1   # JB_CORR_EXACT passes the option check
     assert fwd(args(v_fmt=kvq.KvqFormat.make(4, "token", 128, True, "value"))) == -3
     assert fwd(args(v_fmt=kf)) == -3
     assert fwd(args(o=None)) == -1

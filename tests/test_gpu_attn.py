@@ -72,17 +72,20 @@ def run_oracle(x, w, rows=None, heads=None, *, k_had=True, v_had=True, bits=None
     return O, PS, PR
 
 
+CORR = {0: "none", 1: "taylor", 2: "exact"}
+
+
 def _gather(a, heads, rows):
     return np.stack([a[b, h][rows] for (b, h) in heads])[None]
 
 
-@pytest.mark.parametrize("correction", [1, 0])
+@pytest.mark.parametrize("correction", [1, 0, 2])
 def test_tiny_all_rows(correction):
     w = synth.WORKLOADS["tiny"]
     print(f"attn tiny correction={correction}", flush=True)
     x = synth.draw_all(w)
     O, PS, PR = run_gpu(x, w, correction=correction)
-    Or, PSr, PRr = run_oracle(x, w, correction="taylor" if correction else "none")
+    Or, PSr, PRr = run_oracle(x, w, correction=CORR[correction])
     assert_attention_close(O, Or, f"tiny c={correction}")
     assert_mass_close(PS, PR, PSr, PRr, f"tiny c={correction}")
 
@@ -168,13 +171,13 @@ PERCH = [
 
 
 @pytest.mark.parametrize("shape", PERCH, ids=lambda s: "x".join(str(v) for v in s.values()))
-@pytest.mark.parametrize("bits,correction", [(2, 1), (4, 1), (2, 0)])
+@pytest.mark.parametrize("bits,correction", [(2, 1), (4, 1), (2, 0), (2, 2), (4, 2)])
 def test_per_channel_keys_all_rows(shape, bits, correction):
     w = synth.Workload("perch", **shape, bits=bits, k_dist="t3", k_granularity="channel", seed=11)
     print(f"attn per-channel {shape} bits={bits} correction={correction}", flush=True)
     x = synth.draw_all(w)
     O, PS, PR = run_gpu(x, w, correction=correction)
-    Or, PSr, PRr = run_oracle(x, w, correction="taylor" if correction else "none")
+    Or, PSr, PRr = run_oracle(x, w, correction=CORR[correction])
     assert_attention_close(O, Or, f"perch {shape} b{bits} c{correction}")
     assert_mass_close(PS, PR, PSr, PRr, f"perch {shape} b{bits} c{correction}")
 
@@ -353,3 +356,39 @@ def test_rejects_bad_arguments():
     args = kvq.make_args(q, q, q, kwin, vwin, 128, 2, kf, vf, o=None)  # fwd needs o
     with pytest.raises(kvq.KvqError):
         kvq.jb_attn_fwd(args)
+
+
+# The exact correction sum_c log(sinh(x)/x), x = s q'_c Delta / 2 (an ablation of the
+# second-order form). At the workloads' scale the two forms differ little (per-token keys:
+# about half the output tolerance), so the per-token case also runs at a larger softmax
+# scale (x up to about 1.5), where the oracle's exact and second-order outputs differ by
+# several tolerances and only the exact one matches.
+EXACT_FULL = [("c24", 48), ("c40", 32), ("c40_perch", 32)]
+
+
+@pytest.mark.parametrize("name,nrows", EXACT_FULL)
+def test_exact_correction_sampled_rows(name, nrows):
+    w = synth.WORKLOADS[name]
+    print(f"attn {name} exact correction: full call, oracle on {nrows} rows of one head", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w, correction=2)
+    rows = np.sort(np.concatenate([[0, w.n_q - 1], np.random.default_rng(6).choice(w.n_q, nrows - 2, replace=False)]))
+    heads = [(0, 3)]
+    Or, PSr, PRr = run_oracle(x, w, rows=rows, heads=heads, correction="exact")
+    assert_attention_close(_gather(O, heads, rows), Or, f"{name} exact")
+    assert_mass_close(_gather(PS, heads, rows), _gather(PR, heads, rows), PSr, PRr, f"{name} exact")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_exact_correction_per_token_large_steps(bits):
+    w = synth.Workload("exact", B=1, H=2, d=128, n_q=200, chunk_len=150, n_chunks=3, bits=bits, seed=21)
+    scale = 0.15 if bits == 2 else 0.7  # largest x = s |q'| Delta / 2 about 1.5
+    print(f"attn exact per-token bits={bits} scale={scale}", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w, correction=2, scale=scale)
+    Or, PSr, PRr = run_oracle(x, w, correction="exact", scale=scale)
+    Ot, _, _ = run_oracle(x, w, correction="taylor", scale=scale)
+    gap = np.abs(Ot - Or).max() / np.sqrt(np.mean(Or ** 2))
+    assert gap > 2e-2, f"case does not separate the two forms (max diff {gap:.2e} of rms)"
+    assert_attention_close(O, Or, f"exact per-token b{bits}")
+    assert_mass_close(PS, PR, PSr, PRr, f"exact per-token b{bits}")

@@ -154,3 +154,11 @@ def draw(w: Workload, tensor: str, heads: list[tuple[int, int]] | None = None) -
 def draw_all(w: Workload, heads: list[tuple[int, int]] | None = None) -> dict[str, np.ndarray]:
     """All five inputs of a call: q, k_cache, v_cache, k_cur, v_cur (bf16 bits)."""
     return {t: draw(w, t, heads) for t in TENSOR_IDS}
+
+
+def draw_signs(d: int, seed: int, tensor: str = "k") -> tuple:
+    """A sign vector for a randomized Hadamard rotation H diag(s) (§3 names the
+    randomized rotation): d values of +1/-1, each -1 with probability 1/2, from
+    ``np.random.default_rng([seed, 100 + id])`` with id 0 for keys and 1 for values."""
+    rng = np.random.default_rng([seed, 100 + {"k": 0, "v": 1}[tensor]])
+    return tuple(int(v) for v in np.where(rng.integers(0, 2, d) == 1, -1, 1))

@@ -118,7 +118,7 @@ def reference_call(q_bits, k_cache_bits, v_cache_bits, k_cur_bits, v_cur_bits, *
 def _bias_fn(q, cache, b, h, chunk_len, k_fmt: Format, s, correction):
     if correction == "none":
         return None
-    q_rot = rotate_f64(q) if k_fmt.hadamard else q
+    q_rot = rotate_f64(q, k_fmt.signs) if k_fmt.hadamard else q
     n_chunks = cache["n_chunks"]
     if k_fmt.granularity == "token":
         delta = step_per_token_key(cache["k_scale"][b:b + 1, h:h + 1], chunk_len, n_chunks)[0, 0]

@@ -3,10 +3,12 @@
 The paper rotates keys (and queries) by an orthogonal Hadamard matrix H with
 H^T H = I before quantizing, which spreads channel outliers over all channels
 while leaving every score unchanged, because (Hq)^T (Hk) = q^T k. The rotation
-used here is the plain normalized Sylvester matrix of order d (a power of two),
+is built on the normalized Sylvester matrix of order d (a power of two),
 H[i][j] = (-1)^popcount(i & j) / sqrt(d), which is symmetric and its own
-inverse. (§3 names a randomized Hadamard rotation; the random sign flips are
-not applied here, the plainest reading being one fixed rotation.)
+inverse. §3 names a randomized Hadamard rotation (QuaRot's): R = H diag(s) with
+a fixed sign vector s in {+1, -1}^d, so x' = R x flips the signs of the
+channels with s_c = -1 and then applies H; R^T R = I, (R q)^T (R k) = q^T k,
+and R^{-1} = R^T = diag(s) H. Without a sign vector (s = 1) R is H itself.
 """
 from __future__ import annotations
 
@@ -24,10 +26,35 @@ def sylvester(d: int) -> np.ndarray:
     return h / np.sqrt(d)
 
 
-def rotate_f64(x: np.ndarray) -> np.ndarray:
-    """y = H_d x for every vector along the last axis, in float64 (a plain matmul)."""
+def sign_vector(signs, d: int) -> np.ndarray:
+    """The diagonal s of diag(s) as float64 [d]: all +1 for an empty ``signs``."""
+    if signs is None or len(signs) == 0:
+        return np.ones(d)
+    s = np.asarray(signs, dtype=np.float64)
+    if s.shape != (d,) or not np.all(np.abs(s) == 1):
+        raise ValueError("signs must hold d values of +1 or -1")
+    return s
+
+
+def rotate_f64(x: np.ndarray, signs=()) -> np.ndarray:
+    """y = H_d diag(s) x for every vector along the last axis, in float64 (a plain matmul)."""
     d = x.shape[-1]
-    return np.asarray(x, dtype=np.float64) @ sylvester(d)  # H is symmetric
+    return (np.asarray(x, dtype=np.float64) * sign_vector(signs, d)) @ sylvester(d)  # H is symmetric
+
+
+def unrotate_f64(y: np.ndarray, signs=()) -> np.ndarray:
+    """x = diag(s) H_d y, the inverse of ``rotate_f64``, in float64."""
+    d = y.shape[-1]
+    return (np.asarray(y, dtype=np.float64) @ sylvester(d)) * sign_vector(signs, d)
+
+
+def flip_f32(x: np.ndarray, signs=()) -> np.ndarray:
+    """diag(s) x in float32: an exact negation of the channels with s_c = -1 (the first
+    step of the randomized transform; the float32 butterflies follow)."""
+    x = np.asarray(x, dtype=np.float32)
+    if signs is None or len(signs) == 0:
+        return x
+    return x * sign_vector(signs, x.shape[-1]).astype(np.float32)
 
 
 def scale_f32(d: int) -> np.float32:

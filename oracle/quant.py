@@ -51,7 +51,7 @@ import dataclasses
 
 import numpy as np
 
-from .hadamard import fwht_f32, rotate_f64
+from .hadamard import flip_f32, fwht_f32, unrotate_f64
 
 TOKEN_BLOCK = 64
 
@@ -63,6 +63,7 @@ class Format:
     group: int = 128              # tokens per channel group
     hadamard: bool = True
     role: str = "key"             # "key" (token-major words) | "value" (channel-major blocks)
+    signs: tuple = ()             # randomized rotation H diag(s): d values of +1/-1; () is s = 1
 
 
 def chunk_pad(chunk_len: int) -> int:
@@ -104,7 +105,9 @@ def quantize_chunk(x_bits: np.ndarray, fmt: Format):
     group g covering tokens [g*group, min(n, (g+1)*group)).
     """
     x = bf16_to_f32(x_bits)
-    y = fwht_f32(x) if fmt.hadamard else x
+    if fmt.signs and not fmt.hadamard:
+        raise ValueError("a sign vector needs the Hadamard rotation")
+    y = fwht_f32(flip_f32(x, fmt.signs)) if fmt.hadamard else x
     B, H, n, d = y.shape
     if fmt.granularity == "token":
         codes, delta, z = quantize_lastaxis(y, fmt.bits)
@@ -203,8 +206,8 @@ def pack_window(x_bits: np.ndarray, chunk_len: int, fmt: Format):
 def dequant_window(words, scale, zero, chunk_len: int, n_chunks: int, fmt: Format) -> np.ndarray:
     """Float64 reconstruction of the valid tokens of a window, in the original (un-rotated) basis.
 
-    x_hat' = (code - z) * Delta in the stored basis (Eq. (1)), then x_hat = H x_hat'
-    when the window was rotated.
+    x_hat' = (code - z) * Delta in the stored basis (Eq. (1)), then x_hat = diag(s) H x_hat'
+    when the window was rotated (the inverse of the rotation H diag(s)).
     """
     codes = unpack_key_words(words, fmt.bits) if fmt.role == "key" else unpack_value_words(words, fmt.bits)
     B, H, npad, d = codes.shape
@@ -222,7 +225,7 @@ def dequant_window(words, scale, zero, chunk_len: int, n_chunks: int, fmt: Forma
             dl = scale[:, :, ci * G:(ci + 1) * G, :].astype(np.float64)[:, :, tok_group, :]
             zz = zero[:, :, ci * G:(ci + 1) * G, :].astype(np.float64)[:, :, tok_group, :]
         out[:, :, ci * chunk_len:(ci + 1) * chunk_len, :] = (c - zz) * dl
-    return rotate_f64(out) if fmt.hadamard else out
+    return unrotate_f64(out, fmt.signs) if fmt.hadamard else out
 
 
 def step_per_token_key(scale, chunk_len: int, n_chunks: int) -> np.ndarray:

@@ -139,3 +139,35 @@ def test_mass_check_heavy_tailed_per_channel_keys_reported():
           f"mean shift {shift:+.4f}", flush=True)
     assert np.isfinite([unc, cor, improved, shift]).all()
     assert 0.0 <= improved <= 1.0
+
+
+@pytest.mark.parametrize("granularity", ["token", "channel"])
+def test_randomized_rotation_is_a_channel_sign_flip(granularity):
+    """With R = H diag(s) for keys (and queries) and R_v = H diag(t) for values, the call
+    equals the unrandomized call on s*q, s*k, t*v followed by t*O (the quantizer sees
+    the same float32 values, the scores are unchanged and the values come back through
+    diag(t)). Signs applied to one side only, or a value un-rotation without diag(t),
+    break this."""
+    import dataclasses as dc
+    from bit_kv_cache_kvq_amd import synth
+    from oracle.quant import Format
+    w = synth.Workload("t", B=1, H=2, d=64, n_q=70, chunk_len=90, n_chunks=2, k_granularity=granularity,
+                       group=64, k_dist="t3" if granularity == "channel" else "outlier", seed=4)
+    x = synth.draw_all(w)
+    s = np.array(synth.draw_signs(w.d, 9, "k"))
+    t = np.array(synth.draw_signs(w.d, 9, "v"))
+    kf = Format(2, granularity, 64, True, "key")
+    vf = Format(2, "token", 64, True, "value")
+    flip = lambda bits, sg: synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(bits) * sg.astype(np.float32))
+    O1, PS1, PR1, _ = oracle.reference_call(x["q"], x["k_cache"], x["v_cache"], x["k_cur"], x["v_cur"],
+                                            chunk_len=w.chunk_len, k_fmt=dc.replace(kf, signs=tuple(s)),
+                                            v_fmt=dc.replace(vf, signs=tuple(t)))
+    O0, PS0, PR0, _ = oracle.reference_call(flip(x["q"], s), flip(x["k_cache"], s), flip(x["v_cache"], t),
+                                            flip(x["k_cur"], s), flip(x["v_cur"], t),
+                                            chunk_len=w.chunk_len, k_fmt=kf, v_fmt=vf)
+    np.testing.assert_allclose(O1, O0 * t, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(PS1, PS0, rtol=1e-9, atol=1e-12)
+    # and the signs matter: the same data without them gives another quantized result
+    O2, _, _, _ = oracle.reference_call(x["q"], x["k_cache"], x["v_cache"], x["k_cur"], x["v_cur"],
+                                        chunk_len=w.chunk_len, k_fmt=kf, v_fmt=vf)
+    assert np.abs(O2 - O1).max() > 1e-3

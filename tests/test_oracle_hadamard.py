@@ -103,3 +103,39 @@ def test_fwht_f32_follows_stated_order_bit_exactly(d):
         rev = v.reshape(-1, d)
         h //= 2
     assert np.any(rev * scale_f32(d) != fwht_f32(x))
+
+
+# ---- randomized rotation R = H diag(s) (§3: QuaRot's randomized Hadamard rotation) ----
+from oracle.hadamard import unrotate_f64  # noqa: E402
+
+
+def _popcount_entry(i, c, d):
+    return (-1) ** bin(i & c).count("1") / np.sqrt(d)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_randomized_rotation_columns_closed_form(d):
+    # R e_c = s_c H e_c: column c of R is s_c (-1)^popcount(i & c) / sqrt(d)
+    from bit_kv_cache_kvq_amd.synth import draw_signs
+    s = draw_signs(d, 7)
+    assert set(s) == {-1, 1}
+    for c in (0, 1, 5, d // 2, d - 1):
+        e = np.zeros(d)
+        e[c] = 1.0
+        want = np.array([s[c] * _popcount_entry(i, c, d) for i in range(d)])
+        np.testing.assert_allclose(rotate_f64(e, s), want, atol=1e-15)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_randomized_rotation_orthogonal_inverse_and_dot_products(d):
+    from bit_kv_cache_kvq_amd.synth import draw_signs
+    s = draw_signs(d, 3)
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((20, d))
+    R = rotate_f64(np.eye(d), s)  # rows: R e_c, i.e. R^T
+    np.testing.assert_allclose(R @ R.T, np.eye(d), atol=1e-13)
+    np.testing.assert_allclose(unrotate_f64(rotate_f64(x, s), s), x, atol=1e-13)
+    q, k = x[:10], x[10:]
+    np.testing.assert_allclose(rotate_f64(q, s) @ rotate_f64(k, s).T, q @ k.T, rtol=1e-12, atol=1e-11)
+    # the signs change the rotation (unless all +1)
+    assert np.abs(rotate_f64(x, s) - rotate_f64(x)).max() > 0.1

@@ -91,6 +91,7 @@ struct Params {
   float s;
   int correction;
   int k_had, v_had;
+  uint32_t k_sg[4], v_sg[4];  // randomized rotations H diag(s): bit c set -> channel c negated
   int k_group;  // tokens per key channel group (per-channel keys), else 0
   int n_split;  // workgroups per query block, each over a contiguous share of the tiles
   float* part;  // n_split > 1: partial records [n_split][B*H][n_q][D + 4], else null
@@ -134,6 +135,13 @@ __device__ inline void split16(float x, _Float16& hi, _Float16& lo) {
 }
 
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32); }
+
+// XOR mask that negates channels j and j+1 (j even) of a bf16 pair word, for the sign
+// bits w of channels j0 .. j0+31 (j - j0 = bit index): the randomized rotation's diag(s).
+__device__ inline uint32_t pair_sign_xor(uint32_t w, int bit) {
+  const uint32_t b = w >> bit;
+  return ((b & 1u) << 15) | (((b >> 1) & 1u) << 31);
+}
 
 // log(sinh(x) / x), the logarithm of E[e^(2 x u)] for u uniform on [-1/2, 1/2]: its
 // power series through x^10 (coefficients 2^2n B_2n / (2n (2n)!), omitted terms below
@@ -249,6 +257,12 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   // Rotated query q' = H q / sqrt(d) (or q) of this lane's half: channels HALF h + i.
   auto rotated_query = [&](float* qv) KVQ_INLINE {
     const uint16_t* qrow = p.q + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h;
+    uint32_t sgw[HALF / 32];  // key-rotation signs of this lane's channels HALF h ..
+#pragma unroll
+    for (int k = 0; k < HALF / 32; k++) {
+      sgw[k] = h ? p.k_sg[HALF / 32 + k] : p.k_sg[k];
+      asm volatile("" : "+v"(sgw[k]));  // keeps the per-pair masks here, not hoisted out of the tile loop
+    }
 #pragma unroll
     for (int u = 0; u < HALF / 8; u++) {
       uint4 w = make_uint4(0, 0, 0, 0);
@@ -256,8 +270,10 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        qv[8 * u + 2 * e] = __uint_as_float(ww[e] << 16);
-        qv[8 * u + 2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+        const int j = 8 * u + 2 * e;
+        const uint32_t we = ww[e] ^ pair_sign_xor(sgw[j >> 5], j & 31);
+        qv[j] = __uint_as_float(we << 16);
+        qv[j + 1] = __uint_as_float(we & 0xFFFF0000u);
       }
     }
     if (p.k_had) {
@@ -968,6 +984,15 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
     for (int c = 0; c < CBLK; c++)
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[c][v] *= cn;
+    if (p.v_sg[0] | p.v_sg[1] | p.v_sg[2] | p.v_sg[3]) {  // randomized rotation: diag(t) H
+#pragma unroll
+      for (int c = 0; c < CBLK; c++) {
+        const uint32_t wv = p.v_sg[c] >> (4 * h);
+#pragma unroll
+        for (int v = 0; v < 16; v++)
+          acc[c][v] = __uint_as_float(__float_as_uint(acc[c][v]) ^ (((wv >> ((v & 3) + 8 * (v >> 2))) & 1u) << 31));
+      }
+    }
   };
 
   // Step T of a run of n_t tiles of one kind (tile index U = U0 + T in LDS slot slot0;
@@ -1103,6 +1128,11 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   if (kf.granularity != KVQ_PER_TOKEN && kf.granularity != KVQ_PER_CHANNEL) return KVQ_ERR_UNSUPPORTED;
   if (kf.granularity == KVQ_PER_CHANNEL && kf.group != 64 && kf.group != 128) return KVQ_ERR_UNSUPPORTED;
   if ((kf.hadamard | vf.hadamard) & ~1) return KVQ_ERR_UNSUPPORTED;
+  for (const kvq_format* f : {&kf, &vf}) {
+    const uint32_t any = f->signs[0] | f->signs[1] | f->signs[2] | f->signs[3];
+    if (any && !f->hadamard) return KVQ_ERR_UNSUPPORTED;
+    if (a->d == 64 && (f->signs[2] | f->signs[3])) return KVQ_ERR_UNSUPPORTED;
+  }
   if (a->correction != JB_CORR_NONE && a->correction != JB_CORR_TAYLOR && a->correction != JB_CORR_EXACT)
     return KVQ_ERR_UNSUPPORTED;
   if (a->d != 64 && a->d != 128) return KVQ_ERR_SHAPE;
@@ -1135,19 +1165,26 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   return KVQ_OK;
 }
 
+struct SignWords {
+  uint32_t w[4];
+};
+
 // q' = H q / sqrt(D) in fp32 for every query (keys quantized per channel re-quantize the
 // rotated query at every key group; rotating once per call spares each group the
 // transform). Two lanes per query, half a row each, in the order the attention kernel's
 // own rotation uses: butterflies inside the lane, then across the pair.
 template <int D>
 __global__ __launch_bounds__(256) void jb_rotate_q_kernel(const uint16_t* __restrict__ q, size_t rows,
-                                                          float* __restrict__ qrot) {
+                                                          float* __restrict__ qrot, const SignWords sg) {
   constexpr int HALF = D / 2;
   const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t row = t >> 1;
   const int h = (int)(t & 1);
   const bool ok = row < rows;
   const uint4* src = reinterpret_cast<const uint4*>(q + (ok ? row : 0) * D + HALF * h);
+  uint32_t sgw[HALF / 32];
+#pragma unroll
+  for (int k = 0; k < HALF / 32; k++) sgw[k] = h ? sg.w[HALF / 32 + k] : sg.w[k];
   float qv[HALF];
 #pragma unroll
   for (int u = 0; u < HALF / 8; u++) {
@@ -1155,8 +1192,10 @@ __global__ __launch_bounds__(256) void jb_rotate_q_kernel(const uint16_t* __rest
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-      qv[8 * u + 2 * e] = __uint_as_float(ww[e] << 16);
-      qv[8 * u + 2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+      const int j = 8 * u + 2 * e;
+      const uint32_t we = ww[e] ^ pair_sign_xor(sgw[j >> 5], j & 31);
+      qv[j] = __uint_as_float(we << 16);
+      qv[j + 1] = __uint_as_float(we & 0xFFFF0000u);
     }
   }
 #pragma unroll
@@ -1286,6 +1325,10 @@ int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   p.correction = a->correction;
   p.k_had = a->k_fmt.hadamard;
   p.v_had = a->v_fmt.hadamard;
+  for (int i = 0; i < 4; i++) {
+    p.k_sg[i] = a->k_fmt.signs[i];
+    p.v_sg[i] = a->v_fmt.signs[i];
+  }
   p.k_group = PERCH ? a->k_fmt.group : 0;
   // workspace: [rotated queries][split partials], each 16-byte aligned
   char* ws = static_cast<char*>(a->workspace);
@@ -1294,7 +1337,9 @@ int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   p.part = pl.n_split > 1 ? reinterpret_cast<float*>(ws + pl.qrot_bytes) : nullptr;
   if (pl.qrot_bytes) {
     const size_t rows = (size_t)a->B * a->H * a->n_q;
-    jb_rotate_q_kernel<D><<<(unsigned)((2 * rows + 255) / 256), 256, 0, st>>>(a->q, rows, reinterpret_cast<float*>(ws));
+    jb_rotate_q_kernel<D><<<(unsigned)((2 * rows + 255) / 256), 256, 0, st>>>(a->q, rows, reinterpret_cast<float*>(ws),
+                                                                              SignWords{{a->k_fmt.signs[0], a->k_fmt.signs[1],
+                                                                                         a->k_fmt.signs[2], a->k_fmt.signs[3]}});
   }
   p.o = MASS_ONLY ? nullptr : a->o;
   p.mass_s = a->mass_s;

@@ -16,12 +16,22 @@
 namespace kvq {
 namespace {
 
+// Channel signs of a randomized rotation (bit c of w[c / 32] set: channel c negated).
+struct SignBits {
+  uint32_t w[4];
+};
+
 template <int D>
-__device__ inline void load_token16(const uint16_t* __restrict__ row, int lt, bool valid, float (&y)[16]) {
+__device__ inline void load_token16(const uint16_t* __restrict__ row, int lt, bool valid, const SignBits& sg,
+                                    float (&y)[16]) {
   if (valid) {
     const uint4* p = reinterpret_cast<const uint4*>(row + 16 * lt);
     uint4 a = p[0], b = p[1];
     uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    // this lane's 16 sign bits, moved onto the bf16 sign bits (15, 31) of each channel pair
+    const uint32_t m16 = (sg.w[lt >> 1] >> (16 * (lt & 1))) & 0xFFFFu;
+#pragma unroll
+    for (int i = 0; i < 8; i++) w[i] ^= (((m16 >> (2 * i)) & 1u) << 15) | (((m16 >> (2 * i + 1)) & 1u) << 31);
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       y[2 * i] = __uint_as_float(w[i] << 16);
@@ -115,7 +125,7 @@ __device__ inline void store_key_words(uint32_t* __restrict__ dst_token, int lt,
 // Per-token quantization of one 64-token block of the padded chunk.
 template <int D, int BITS, int ROLE>
 __global__ __launch_bounds__(64 * D / 16) void pack_token_kernel(
-    const uint16_t* __restrict__ x, int n, int n_chunks, int chunk_idx, int hadamard,
+    const uint16_t* __restrict__ x, int n, int n_chunks, int chunk_idx, int hadamard, const SignBits sg,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint16_t* __restrict__ zero) {
   constexpr int LPT = D / 16;            // lanes per token
   constexpr int CPW = 32 / BITS;         // codes per word
@@ -129,7 +139,7 @@ __global__ __launch_bounds__(64 * D / 16) void pack_token_kernel(
   const size_t n_tot = (size_t)n_chunks * cp;
 
   float y[16];
-  load_token16<D>(x + (bh * n + (valid ? t : 0)) * D, lt, valid, y);
+  load_token16<D>(x + (bh * n + (valid ? t : 0)) * D, lt, valid, sg, y);
   if (hadamard) fwht_rows<D>(y, lt);
 
   float mn = y[0], mx = y[0];
@@ -177,7 +187,7 @@ __global__ __launch_bounds__(64 * D / 16) void pack_token_kernel(
 // Per-channel key quantization: one workgroup per group of GROUP tokens of the chunk.
 template <int D, int BITS, int GROUP>
 __global__ __launch_bounds__(GROUP * D / 16) void pack_channel_kernel(
-    const uint16_t* __restrict__ x, int n, int n_chunks, int chunk_idx, int hadamard,
+    const uint16_t* __restrict__ x, int n, int n_chunks, int chunk_idx, int hadamard, const SignBits sg,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint16_t* __restrict__ zero) {
   constexpr int LPT = D / 16;
   constexpr int CPW = 32 / BITS;
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(GROUP * D / 16) void pack_channel_kernel(
   const int n_valid = min(GROUP, n - t0);
 
   float y[16];
-  load_token16<D>(x + (bh * n + (valid ? t : 0)) * D, lt, valid, y);
+  load_token16<D>(x + (bh * n + (valid ? t : 0)) * D, lt, valid, sg, y);
   if (hadamard) fwht_rows<D>(y, lt);
 #pragma unroll
   for (int i = 0; i < 16; i++) s_y[tl][16 * lt + i] = y[i];
@@ -231,6 +241,7 @@ int validate_format(const kvq_format* f) {
   if (!f) return KVQ_ERR_NULL;
   if (f->bits != 2 && f->bits != 4) return KVQ_ERR_UNSUPPORTED;
   if (f->hadamard != 0 && f->hadamard != 1) return KVQ_ERR_UNSUPPORTED;
+  if (!f->hadamard && (f->signs[0] | f->signs[1] | f->signs[2] | f->signs[3])) return KVQ_ERR_UNSUPPORTED;
   if (f->role != KVQ_ROLE_KEY && f->role != KVQ_ROLE_VALUE) return KVQ_ERR_UNSUPPORTED;
   if (f->granularity == KVQ_PER_TOKEN) return KVQ_OK;
   if (f->granularity != KVQ_PER_CHANNEL) return KVQ_ERR_UNSUPPORTED;
@@ -243,22 +254,23 @@ template <int D, int BITS>
 int launch_pack(const uint16_t* x, int B, int H, int n, const kvq_format* f, int n_chunks, int chunk_idx,
                 uint32_t* codes, uint16_t* scale, uint16_t* zero, hipStream_t st) {
   const dim3 bh(1, (unsigned)(B * H));
+  const SignBits sg = {{f->signs[0], f->signs[1], f->signs[2], f->signs[3]}};
   if (f->granularity == KVQ_PER_TOKEN) {
     const dim3 grid((unsigned)(chunk_pad(n) / kTokenBlock), (unsigned)(B * H));
     if (f->role == KVQ_ROLE_KEY)
       pack_token_kernel<D, BITS, KVQ_ROLE_KEY><<<grid, 64 * D / 16, 0, st>>>(x, n, n_chunks, chunk_idx, f->hadamard,
-                                                                             codes, scale, zero);
+                                                                             sg, codes, scale, zero);
     else
       pack_token_kernel<D, BITS, KVQ_ROLE_VALUE><<<grid, 64 * D / 16, 0, st>>>(x, n, n_chunks, chunk_idx,
-                                                                               f->hadamard, codes, scale, zero);
+                                                                               f->hadamard, sg, codes, scale, zero);
   } else {
     const dim3 grid((unsigned)((n + f->group - 1) / f->group), (unsigned)(B * H));
     if (f->group == 64)
-      pack_channel_kernel<D, BITS, 64><<<grid, 64 * D / 16, 0, st>>>(x, n, n_chunks, chunk_idx, f->hadamard, codes,
-                                                                     scale, zero);
+      pack_channel_kernel<D, BITS, 64><<<grid, 64 * D / 16, 0, st>>>(x, n, n_chunks, chunk_idx, f->hadamard, sg,
+                                                                     codes, scale, zero);
     else
       pack_channel_kernel<D, BITS, 128><<<grid, 128 * D / 16, 0, st>>>(x, n, n_chunks, chunk_idx, f->hadamard,
-                                                                       codes, scale, zero);
+                                                                       sg, codes, scale, zero);
   }
   (void)bh;
   return launch_status();
@@ -295,6 +307,7 @@ extern "C" int kvq_pack(const uint16_t* x, int32_t B, int32_t H, int32_t n, int3
   if (!x || !codes || !scale || !zero) return KVQ_ERR_NULL;
   if (B < 1 || H < 1 || n < 1 || n_chunks < 1 || chunk_idx < 0 || chunk_idx >= n_chunks) return KVQ_ERR_SHAPE;
   if (d != 64 && d != 128) return KVQ_ERR_SHAPE;
+  if (d == 64 && (fmt->signs[2] | fmt->signs[3])) return KVQ_ERR_UNSUPPORTED;
   if ((long long)B * H > 65535) return KVQ_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scale) || !aligned16(zero)) return KVQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -32,12 +32,30 @@ class KvqError(RuntimeError):
 
 class KvqFormat(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("granularity", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("hadamard", ctypes.c_int32), ("role", ctypes.c_int32)]
+                ("hadamard", ctypes.c_int32), ("role", ctypes.c_int32), ("signs", ctypes.c_uint32 * 4)]
 
     @classmethod
-    def make(cls, bits=2, granularity="token", group=128, hadamard=True, role="key"):
-        return cls(bits, {"token": KVQ_PER_TOKEN, "channel": KVQ_PER_CHANNEL}[granularity], group,
-                   int(bool(hadamard)), {"key": KVQ_ROLE_KEY, "value": KVQ_ROLE_VALUE}[role])
+    def make(cls, bits=2, granularity="token", group=128, hadamard=True, role="key", signs=None):
+        """signs: None, or d values of +1/-1 (the randomized rotation H diag(s))."""
+        f = cls(bits, {"token": KVQ_PER_TOKEN, "channel": KVQ_PER_CHANNEL}[granularity], group,
+                int(bool(hadamard)), {"key": KVQ_ROLE_KEY, "value": KVQ_ROLE_VALUE}[role])
+        for i, w in enumerate(sign_words(signs)):
+            f.signs[i] = w
+        return f
+
+
+def sign_words(signs):
+    """d values of +1/-1 -> the 4-word mask of kvq_format.signs (bit c set: s_c = -1)."""
+    words = [0, 0, 0, 0]
+    if signs is None:
+        return words
+    signs = list(signs)
+    if len(signs) > 128 or any(v not in (1, -1) for v in signs):
+        raise ValueError("signs must be at most 128 values of +1 or -1")
+    for c, v in enumerate(signs):
+        if v == -1:
+            words[c // 32] |= 1 << (c % 32)
+    return words
 
 
 class JbAttnArgs(ctypes.Structure):

@@ -74,13 +74,21 @@ enum { JB_CORR_NONE = 0, JB_CORR_TAYLOR = 1, JB_CORR_EXACT = 2 };
  * (correctly rounded); Delta = fp16(d32) (nearest even); if Delta == 0 then scale =
  * zero = +0 and codes 0; else z = rint(-mn/Delta) + 0 (half-even, -0 -> +0, not
  * clamped); code = clamp(rint(y/Delta) + z, 0, 2^bits - 1); scale = Delta, zero = fp16(z)
- * (exact for |z| <= 2048). Reconstruction: x_hat' = (code - zero) * scale, x_hat = H x_hat'. */
+ * (exact for |z| <= 2048). Reconstruction: x_hat' = (code - zero) * scale, x_hat = H x_hat'.
+ *
+ * Randomized rotation (§3 names QuaRot's randomized Hadamard rotation): with signs set,
+ * the rotation is R = H diag(s), s_c = -1 where bit c % 32 of signs[c / 32] is set: those
+ * channels are negated (exactly) before the butterflies, and x_hat = diag(s) H x_hat'.
+ * Attention rotates the queries with the key format's R and un-rotates its output with
+ * the value format's. All-zero signs give R = H. */
 typedef struct {
   int32_t bits;        /* 2 or 4 */
   int32_t granularity; /* KVQ_PER_TOKEN, or KVQ_PER_CHANNEL (role KEY only) */
   int32_t group;       /* tokens per channel group: 64 or 128 (KVQ_PER_CHANNEL only) */
   int32_t hadamard;    /* 1: rotate by the normalized Sylvester-Hadamard matrix first */
   int32_t role;        /* KVQ_ROLE_KEY or KVQ_ROLE_VALUE: selects the code layout */
+  uint32_t signs[4];   /* channel sign mask of a randomized rotation (hadamard = 1 only;
+                          bits at channels >= d must be 0); all zero: none */
 } kvq_format;
 
 /* Tokens per chunk after padding to a multiple of 64. */
@@ -97,7 +105,8 @@ int kvq_window_elems(const kvq_format* fmt, int32_t B, int32_t H, int32_t d, int
  *   codes, scale, zero  the window arrays described at kvq_format; only chunk
  *          chunk_idx's slice (its padded tokens, or its channel groups) is written.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (B,H,n < 1; d not 64/128; chunk_idx outside
- * [0, n_chunks)), KVQ_ERR_UNSUPPORTED (bits, granularity/role/group combination),
+ * [0, n_chunks)), KVQ_ERR_UNSUPPORTED (bits, granularity/role/group combination, signs
+ * without hadamard or past channel d),
  * KVQ_ERR_ALIGN, KVQ_ERR_HIP. */
 int kvq_pack(const uint16_t* x, int32_t B, int32_t H, int32_t n, int32_t d, const kvq_format* fmt,
              int32_t n_chunks, int32_t chunk_idx, uint32_t* codes, uint16_t* scale, uint16_t* zero,
@@ -157,7 +166,8 @@ typedef struct {
  * 2^15 nats.
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (also when one head's cached codes exceed 2^31 - 1
  * bytes), KVQ_ERR_UNSUPPORTED (mixed bits, value per-channel, wrong roles, group not
- * 64/128), KVQ_ERR_ALIGN (also a misaligned workspace that a split would use), KVQ_ERR_HIP. */
+ * 64/128, signs without hadamard or past channel d), KVQ_ERR_ALIGN (also a misaligned
+ * workspace that a split would use), KVQ_ERR_HIP. */
 int jb_attn_fwd(const jb_attn_args* a, void* stream);
 
 /* Attention masses only (Fig. 2): writes mass_s and mass_r; o and values are not read. */

@@ -39,8 +39,9 @@ def test_library_exports_every_declared_symbol(kvq):
 
 
 def test_struct_layouts_match_header(kvq):
-    # five int32 fields; the attention struct has no hidden padding surprises on x86-64
-    assert ctypes.sizeof(kvq.KvqFormat) == 20
+    # five int32 fields and four uint32 sign words; no hidden padding on x86-64
+    assert ctypes.sizeof(kvq.KvqFormat) == 36
+    assert kvq.KvqFormat.signs.offset == 20
     off = kvq.JbAttnArgs.q.offset
     assert off == 32  # 7 int32 = 28 bytes, pointer aligned to 8
 
@@ -79,6 +80,10 @@ def test_pack_validation_without_launch(kvq):
     assert call(kvq.KvqFormat.make(2, "channel", 128, True, "value"), p, 1, 1, 64, 128, 1, 0, p, p, p, None) == -3
     q = ctypes.c_void_p(18)
     assert call(f, q, 1, 1, 64, 128, 1, 0, p, p, p, None) == -4              # misaligned
+    nosign = kvq.KvqFormat.make(2, "token", 128, False, "key", [-1] + [1] * 127)
+    assert call(nosign, p, 1, 1, 64, 128, 1, 0, p, p, p, None) == -3         # signs without rotation
+    wide = kvq.KvqFormat.make(2, "token", 128, True, "key", [1] * 127 + [-1])
+    assert call(wide, p, 1, 1, 64, 64, 1, 0, p, p, p, None) == -3            # sign past channel d
 
 
 def test_attn_validation_without_launch(kvq):
@@ -103,6 +108,9 @@ def test_attn_validation_without_launch(kvq):
     assert fwd(args(correction=7)) == -3
     assert fwd(args(correction=3)) == -3
     assert fwd(args(correction=2, o=None)) == -1   # JB_CORR_EXACT passes the option check
+    assert fwd(args(k_fmt=kvq.KvqFormat.make(2, "token", 128, False, "key", [-1] * 128))) == -3
+    assert fwd(args(d=64, v_fmt=kvq.KvqFormat.make(2, "token", 128, True, "value", [1] * 127 + [-1]))) == -3
+    assert fwd(args(k_fmt=kvq.KvqFormat.make(2, "token", 128, True, "key", [-1] * 128), o=None)) == -1
     assert fwd(args(v_fmt=kvq.KvqFormat.make(4, "token", 128, True, "value"))) == -3
     assert fwd(args(v_fmt=kf)) == -3
     assert fwd(args(o=None)) == -1
@@ -112,3 +120,11 @@ def test_attn_validation_without_launch(kvq):
     assert fwd(args(softmax_scale=-1.0)) == -2
     assert mass(args()) == -1                   # mass needs mass_s / mass_r
     assert lib.jb_attn_workspace_bytes(ctypes.byref(args())) == 0   # no device here: no split planned
+
+
+def test_sign_words(kvq):
+    assert kvq.sign_words(None) == [0, 0, 0, 0]
+    assert kvq.sign_words([1, -1, 1, -1] + [1] * 60) == [0b1010, 0, 0, 0]
+    assert kvq.sign_words([1] * 100 + [-1] + [1] * 27) == [0, 0, 0, 1 << 4]
+    with pytest.raises(ValueError):
+        kvq.sign_words([0] * 64)

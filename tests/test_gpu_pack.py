@@ -18,17 +18,17 @@ def _kvq():
     return kvq
 
 
-def _check_window(x_bits, chunk_len, bits, gran, group, had, role, heads=None, label=""):
+def _check_window(x_bits, chunk_len, bits, gran, group, had, role, heads=None, label="", signs=()):
     kvq = _kvq()
     B, H, n, d = x_bits.shape
-    print(f"pack {label}: B={B} H={H} n={n} d={d} chunk={chunk_len} bits={bits} {gran}/{group} had={had} {role}",
-          flush=True)
-    fmt = kvq.KvqFormat.make(bits, gran, group, had, role)
+    print(f"pack {label}: B={B} H={H} n={n} d={d} chunk={chunk_len} bits={bits} {gran}/{group} had={had} {role}"
+          f"{' signs' if signs else ''}", flush=True)
+    fmt = kvq.KvqFormat.make(bits, gran, group, had, role, signs or None)
     codes, scale, zero = kvq.pack_window(dev(x_bits), chunk_len, fmt)
     import torch
     torch.cuda.synchronize()
     heads = heads or [(b, h) for b in range(B) for h in range(H)]
-    ofmt = Format(bits, gran, group, bool(had), role)
+    ofmt = Format(bits, gran, group, bool(had), role, tuple(signs))
     gw, gs, gz = host_u32(codes), host_u16(scale), host_u16(zero)
     for (b, h) in heads:
         w, s, z = pack_window(x_bits[b:b + 1, h:h + 1], chunk_len, ofmt)
@@ -101,3 +101,14 @@ def test_pack_rejects_bad_arguments():
         kvq.kvq_pack(x, kvq.KvqFormat.make(2, "channel", 128, True, "value"), 1, 0, codes, scale, zero)
     with pytest.raises(kvq.KvqError):
         kvq.kvq_pack(x[..., :96].contiguous(), fmt, 1, 0, codes, scale, zero)   # d = 96
+
+
+# randomized rotation H diag(s): codes, steps and zero points bit-exact with the oracle
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bits,gran,role", [(2, "token", "key"), (4, "token", "value"), (2, "channel", "key")])
+def test_pack_randomized_rotation(d, bits, gran, role):
+    w = synth.Workload("signs", B=1, H=2, d=d, n_q=64, chunk_len=200, n_chunks=2, seed=8,
+                       k_dist="t3" if gran == "channel" else "outlier")
+    x = synth.draw(w, "k_cache")
+    s = synth.draw_signs(d, 5, "k")
+    _check_window(x, w.chunk_len, bits, gran, 128, 1, role, None, f"signs d{d}", signs=s)

@@ -52,6 +52,19 @@ def traffic_from_profile():
     return float(m_bytes.group(1))
 
 
+def window_memory(w):
+    """Device bytes of this workload's cached window (K and V) in INT2, INT4 and bf16: the
+    memory a fixed window takes, or the window a fixed budget holds (§1)."""
+    from bit_kv_cache_kvq_amd import kvq, window
+    def kv(bits):
+        kf = kvq.KvqFormat.make(bits, w.k_granularity, w.group, True, "key")
+        vf = kvq.KvqFormat.make(bits, "token", w.group, True, "value")
+        return sum(window.window_bytes(f, w.B, w.H, w.d, w.chunk_len, w.n_chunks) for f in (kf, vf))
+    b2, b4, b16 = kv(2), kv(4), 2 * w.B * w.H * w.n_chunks * w.chunk_len * w.d * 2
+    return {"int2_bytes": b2, "int4_bytes": b4, "bf16_bytes": b16, "int2_over_int4": round(b2 / b4, 4),
+            "int2_over_bf16": round(b2 / b16, 4)}
+
+
 def cpu_baseline(w, x, heads, kf_o, vf_o, correction="taylor"):
     """Time the oracle (as it stands) on `heads`: pack of the current chunk + attention."""
     import numpy as np
@@ -195,6 +208,7 @@ def main():
                    "parallelism": "none (1 GPU)", "split_workspace_bytes": a.workspace_bytes},
         "attn_ms": round(attn_ms, 4),
         "cache_GBps": round(cache_bytes / (attn_ms * 1e-3) / 1e9, 2),
+        "window_memory": window_memory(w),
         "cache_frac_hbm": round(cache_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
         "pack": {"ms": round(pack_ms, 4), "algorithmic_bytes": pack_bytes,
                  "GBps": round(pack_bytes / (pack_ms * 1e-3) / 1e9, 1),

@@ -78,6 +78,7 @@ constexpr float kQFix = 32639.f;  // |q_f| <= 32639 keeps hi = (q_f + 128) >> 8 
 
 struct Params {
   int B, H, n_q, n_r, chunk_len, n_chunks, cp;
+  int n_wchunks;  // chunks per head in the window arrays (their per-head stride), >= n_chunks
   int n_qblk;
   const uint16_t* q;
   const uint16_t* k_cur;
@@ -413,13 +414,14 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   const int tiles_per_chunk = p.cp / kBN;
   const int n_ct = p.n_chunks * tiles_per_chunk;  // cached tiles
   const int n_rt = (p.n_r + kBN - 1) / kBN;       // current-chunk tiles
-  const size_t n_tot = (size_t)p.n_chunks * p.cp;
-  const uint32_t* kc_base = p.k_codes + (size_t)bh * n_tot * KW;
-  const uint32_t* vc_base = p.v_codes + (size_t)bh * (n_tot / kBN) * VWT;
-  const uint16_t* ks_base = p.k_scale + (size_t)bh * n_tot;
-  const uint16_t* kz_base = p.k_zero + (size_t)bh * n_tot;
-  const uint16_t* vs_base = p.v_scale + (size_t)bh * n_tot;
-  const uint16_t* vz_base = p.v_zero + (size_t)bh * n_tot;
+  const size_t n_tot = (size_t)p.n_chunks * p.cp;     // cached tokens attended (padded)
+  const size_t n_str = (size_t)p.n_wchunks * p.cp;    // per-head stride of the window arrays
+  const uint32_t* kc_base = p.k_codes + (size_t)bh * n_str * KW;
+  const uint32_t* vc_base = p.v_codes + (size_t)bh * (n_str / kBN) * VWT;
+  const uint16_t* ks_base = p.k_scale + (size_t)bh * n_str;
+  const uint16_t* kz_base = p.k_zero + (size_t)bh * n_str;
+  const uint16_t* vs_base = p.v_scale + (size_t)bh * n_str;
+  const uint16_t* vz_base = p.v_zero + (size_t)bh * n_str;
   const uint16_t* kr_base = p.k_cur + (size_t)bh * p.n_r * D;
   const uint16_t* vr_base = p.v_cur + (size_t)bh * p.n_r * D;
   // descriptors of this head's cached window (the byte sizes fit 31 bits: checked on the host)
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
         // per-channel keys: the step row (lanes 0 .. D/8-1) and zero-point row of the
         // tile's key group, 16 bytes per lane
         const int ci = U / tiles_per_chunk, tt = U % tiles_per_chunk;
-        const size_t row = ((size_t)bh * p.n_chunks * k_gpc + (size_t)ci * k_gpc + tt / k_tpg) * D;
+        const size_t row = ((size_t)bh * p.n_wchunks * k_gpc + (size_t)ci * k_gpc + tt / k_tpg) * D;
         const uint16_t* src = tid < D / 8 ? p.k_scale : p.k_zero;
         gpre = reinterpret_cast<const uint4*>(src + row)[tid % (D / 8)];
       }
@@ -1139,6 +1141,7 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   if (a->B < 1 || a->H < 1 || a->n_q < 1 || a->n_r < 0 || a->chunk_len < 1 || a->n_chunks < 0)
     return KVQ_ERR_SHAPE;
   if ((long long)a->n_chunks * a->chunk_len + a->n_r < 1) return KVQ_ERR_SHAPE;
+  if (a->window_chunks < 0 || (a->window_chunks > 0 && a->window_chunks < a->n_chunks)) return KVQ_ERR_SHAPE;
   if (!(a->softmax_scale >= 0.f) || isinf(a->softmax_scale)) return KVQ_ERR_SHAPE;
   // the kernel addresses one head's cached codes through 32-bit buffer offsets
   if ((long long)a->n_chunks * chunk_pad(a->chunk_len) * a->d * kf.bits / 8 > 0x7FFFFFFFLL) return KVQ_ERR_SHAPE;
@@ -1310,6 +1313,7 @@ int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   p.n_r = a->n_r;
   p.chunk_len = a->chunk_len;
   p.n_chunks = a->n_chunks;
+  p.n_wchunks = a->window_chunks > 0 ? a->window_chunks : a->n_chunks;
   p.cp = chunk_pad(a->chunk_len);
   p.n_qblk = pl.n_qblk;
   p.q = a->q;

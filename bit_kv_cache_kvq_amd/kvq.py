@@ -68,7 +68,8 @@ class JbAttnArgs(ctypes.Structure):
                 ("k_fmt", KvqFormat), ("v_fmt", KvqFormat),
                 ("softmax_scale", ctypes.c_float), ("correction", ctypes.c_int32),
                 ("o", ctypes.c_void_p), ("mass_s", ctypes.c_void_p), ("mass_r", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("window_chunks", ctypes.c_int32)]
 
 
 def _load():
@@ -169,8 +170,9 @@ def kvq_pack(x, fmt: KvqFormat, n_chunks: int, chunk_idx: int, codes, scale, zer
 
 
 def make_args(q, k_cur, v_cur, k_window, v_window, chunk_len, n_chunks, k_fmt, v_fmt, o=None, mass_s=None,
-              mass_r=None, correction=JB_CORR_TAYLOR, softmax_scale=0.0):
-    """Fill a JbAttnArgs from tensors. k_window / v_window are (codes, scale, zero) or None.
+              mass_r=None, correction=JB_CORR_TAYLOR, softmax_scale=0.0, window_chunks=0):
+    """Fill a JbAttnArgs from tensors. k_window / v_window are (codes, scale, zero) or None;
+    window_chunks is their per-head chunk capacity when it exceeds n_chunks (0: n_chunks).
 
     The workspace is left empty (the call then runs unsplit); attach_workspace adds it."""
     B, H, n_q, d = q.shape
@@ -182,7 +184,7 @@ def make_args(q, k_cur, v_cur, k_window, v_window, chunk_len, n_chunks, k_fmt, v
     return JbAttnArgs(B, H, d, n_q, n_r, chunk_len, n_chunks, _ptr(q), _ptr(k_cur), _ptr(v_cur),
                       _ptr(kw[0]), _ptr(kw[1]), _ptr(kw[2]), _ptr(vw[0]), _ptr(vw[1]), _ptr(vw[2]),
                       k_fmt, v_fmt, float(softmax_scale), int(correction), _ptr(o), _ptr(mass_s), _ptr(mass_r),
-                      None, 0)
+                      None, 0, int(window_chunks))
 
 
 def jb_attn_fwd(args: JbAttnArgs, stream=None):

@@ -153,6 +153,12 @@ typedef struct {
   float* mass_r;              /* fp32 [B, H, n_q]: as mass_s */
   void* workspace;            /* device, 16-byte aligned, caller-owned; may be NULL (see below) */
   size_t workspace_bytes;     /* its size in bytes */
+  int32_t window_chunks;      /* chunks per head the window arrays are laid out for (their
+                                 stride), >= n_chunks; 0 means n_chunks. A sliding window
+                                 kept as a ring of window_chunks slots (kvq_pack's n_chunks
+                                 and chunk_idx) passes the slots in use as chunks 0 ..
+                                 n_chunks - 1 in any order: the attention does not depend on
+                                 the order of the cached tokens. */
 } jb_attn_args;
 
 /* Corrected attention forward: writes o and, if given, mass_s/mass_r.

@@ -44,6 +44,7 @@ def test_struct_layouts_match_header(kvq):
     assert kvq.KvqFormat.signs.offset == 20
     off = kvq.JbAttnArgs.q.offset
     assert off == 32  # 7 int32 = 28 bytes, pointer aligned to 8
+    assert kvq.JbAttnArgs.window_chunks.offset == kvq.JbAttnArgs.workspace_bytes.offset + 8
 
 
 def test_geometry(kvq):
@@ -107,6 +108,9 @@ def test_attn_validation_without_launch(kvq):
     assert fwd(args(n_chunks=0, n_r=0)) == -2
     assert fwd(args(correction=7)) == -3
     assert fwd(args(correction=3)) == -3
+    assert fwd(args(window_chunks=-1)) == -2
+    assert fwd(args(n_chunks=2, window_chunks=1)) == -2     # fewer slots than chunks attended
+    assert fwd(args(n_chunks=2, window_chunks=3, o=None)) == -1
     assert fwd(args(correction=2, o=None)) == -1   # JB_CORR_EXACT passes the option check
     assert fwd(args(k_fmt=kvq.KvqFormat.make(2, "token", 128, False, "key", [-1] * 128))) == -3
     assert fwd(args(d=64, v_fmt=kvq.KvqFormat.make(2, "token", 128, True, "value", [1] * 127 + [-1]))) == -3
@@ -128,3 +132,18 @@ def test_sign_words(kvq):
     assert kvq.sign_words([1] * 100 + [-1] + [1] * 27) == [0, 0, 0, 1 << 4]
     with pytest.raises(ValueError):
         kvq.sign_words([0] * 64)
+
+
+def test_window_ring_bookkeeping(kvq):
+    from bit_kv_cache_kvq_amd import window
+    assert [window.ring_slot(t, 3) for t in range(7)] == [0, 1, 2, 0, 1, 2, 0]
+    with pytest.raises(ValueError):
+        window.ring_slot(0, 0)
+    # c40 window (8 chunks of 4680 tokens, 40 heads, d 128): INT2 K+V against INT4 and bf16
+    fk = lambda b: kvq.KvqFormat.make(b, "token", 128, True, "key")
+    fv = lambda b: kvq.KvqFormat.make(b, "token", 128, True, "value")
+    w2 = window.window_bytes(fk(2), 1, 40, 128, 4680, 8) + window.window_bytes(fv(2), 1, 40, 128, 4680, 8)
+    w4 = window.window_bytes(fk(4), 1, 40, 128, 4680, 8) + window.window_bytes(fv(4), 1, 40, 128, 4680, 8)
+    bf16 = 2 * 40 * 8 * 4680 * 128 * 2
+    assert w2 == 2 * 40 * 8 * 4736 * (32 + 4)      # padded tokens: 32 code bytes + fp16 step and zero
+    assert abs(w2 / w4 - 0.529) < 1e-3 and w2 / bf16 < 0.15

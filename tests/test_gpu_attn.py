@@ -460,3 +460,46 @@ def test_randomized_rotation_c40_sampled_rows():
     Or, PSr, PRr = run_oracle(x, w, rows=rows, heads=heads, k_signs=ks, v_signs=vs)
     assert_attention_close(_gather(O, heads, rows), Or, "c40 signs")
     assert_mass_close(_gather(PS, heads, rows), _gather(PR, heads, rows), PSr, PRr, "c40 signs")
+
+
+# A sliding window kept as a ring (bit_kv_cache_kvq_amd.window): six chunks are generated
+# in turn, each attending to the previous ones (at most three) and to itself, twice (two
+# denoising steps with different queries over the same packed window); a finished chunk's
+# keys and values are then packed into the next slot. Every call is checked against the
+# oracle on the chronological window: partly filled (fewer chunks than slots, so the
+# arrays' stride differs from the chunks attended) and wrapped (slots out of order).
+@pytest.mark.parametrize("gran", ["token", "channel"])
+def test_sliding_window_ring(gran):
+    from bit_kv_cache_kvq_amd import window
+    kvq = _kvq()
+    B, H, d, L, cap, T = 1, 2, 128, 100, 3, 6
+    base = synth.Workload("ring", B=B, H=H, d=d, n_q=L, chunk_len=L, n_chunks=1, k_granularity=gran, group=64,
+                          k_dist="t3" if gran == "channel" else "outlier")
+    kf, vf = lib_formats(base)
+    okf, ovf = oracle_formats(base)
+    win = window.ChunkWindow(B, H, d, L, cap, kf, vf)
+    hist = []  # finished chunks' (k, v) bf16 bits, in order
+    for t in range(T):
+        x = synth.draw_all(base.replace(seed=100 + t))
+        for step in range(2):
+            qb = x["q"] if step == 0 else synth.draw(base.replace(seed=200 + t), "q")
+            print(f"attn ring {gran}: chunk {t} step {step} window {win.n_chunks} pushed {win.pushed}", flush=True)
+            o = torch.empty((B, H, L, d), dtype=torch.float32, device="cuda")
+            ms = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+            mr = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+            q, kr, vr = dev(qb), dev(x["k_cur"]), dev(x["v_cur"])
+            a = win.args(q, kr, vr, o=o, mass_s=ms, mass_r=mr)
+            ws = kvq.attach_workspace(a)
+            kvq.jb_attn_fwd(a)
+            torch.cuda.synchronize()
+            del ws
+            lo = max(0, t - cap)
+            kc = np.concatenate([k for k, _ in hist[lo:t]], axis=2) if t else np.zeros((B, H, 0, d), np.uint16)
+            vc = np.concatenate([v for _, v in hist[lo:t]], axis=2) if t else np.zeros((B, H, 0, d), np.uint16)
+            Or, PSr, PRr, _ = oracle.reference_call(qb, kc, vc, x["k_cur"], x["v_cur"], chunk_len=L, k_fmt=okf,
+                                                    v_fmt=ovf)
+            assert_attention_close(o.cpu().numpy(), Or, f"ring {gran} t{t} s{step}")
+            assert_mass_close(ms.cpu().numpy(), mr.cpu().numpy(), PSr, PRr, f"ring {gran} t{t} s{step}")
+        win.push(kr, vr)
+        hist.append((x["k_cur"], x["v_cur"]))
+    assert win.n_chunks == cap and win.pushed == T

@@ -61,6 +61,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -75,6 +76,7 @@ constexpr float kMaskLogit = 65504.f;  // subtracted from padded keys' logits (l
 constexpr float kD2Scale = 64.f;     // Delta^2 is carried as Delta^2 / 64 (fp16 range)
 
 constexpr float kQFix = 32639.f;  // |q_f| <= 32639 keeps hi = (q_f + 128) >> 8 in int8
+constexpr float kRoundMagic = 12582912.f;  // 1.5 2^23: adding it rounds |x| < 2^22 to an integer
 
 struct Params {
   int B, H, n_q, n_r, chunk_len, n_chunks, cp;
@@ -502,20 +504,24 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         // four codes of this word: q_f = rint(q~ / sigma), split into hi = (q_f + 128) >> 8
-        // and lo = q_f - 256 hi as int16 pairs, whose low bytes form the two operand words
-        float qf[4];
+        // and lo = q_f - 256 hi. fma(x, inv, 1.5 2^23) rounds x inv to an integer in the
+        // low mantissa bits (|x inv| < 2^22), so the low 16 bits of the float are q_f as
+        // int16; lo is q_f's low byte and hi is byte 1 of q_f + 128
+        uint32_t fb[4];
 #pragma unroll
         for (int b = 0; b < 4; b++) {
           const int c = kperm<BITS>(j, b);
-          qf[b] = __builtin_rintf(qv[16 * kk + c] * inv);
-          zs = fmaf(qf[b], (float)zt[c], zs);
+          const float f = fmaf(qv[16 * kk + c], inv, kRoundMagic);
+          fb[b] = __float_as_uint(f);
+          zs = fmaf(f - kRoundMagic, (float)zt[c], zs);  // q_f, exact
         }
-        const s16x2 p0 = __builtin_amdgcn_cvt_pk_i16((int)qf[0], (int)qf[1]);
-        const s16x2 p1 = __builtin_amdgcn_cvt_pk_i16((int)qf[2], (int)qf[3]);
-        const s16x2 h0 = (p0 + (short)128) >> (short)8, h1 = (p1 + (short)128) >> (short)8;
-        const s16x2 l0 = p0 - (h0 << (short)8), l1 = p1 - (h1 << (short)8);
-        qhi[kk][j] = (int)__builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, h1), __builtin_bit_cast(uint32_t, h0), 0x06040200u);
-        qlo[kk][j] = (int)__builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, l1), __builtin_bit_cast(uint32_t, l0), 0x06040200u);
+        const uint32_t p0 = __builtin_amdgcn_perm(fb[1], fb[0], 0x05040100u);  // int16 pairs
+        const uint32_t p1 = __builtin_amdgcn_perm(fb[3], fb[2], 0x05040100u);
+        const u16x2 off = {(unsigned short)128, (unsigned short)128};
+        const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, p0) + off);
+        const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, p1) + off);
+        qhi[kk][j] = (int)__builtin_amdgcn_perm(h1, h0, 0x07050301u);
+        qlo[kk][j] = (int)__builtin_amdgcn_perm(p1, p0, 0x06040200u);
       }
     }
     zs += xor32(zs);

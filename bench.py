@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--correction", type=int, default=1, choices=sorted(CORR_NAMES),
                     help="0 none, 1 second-order Taylor (the headline), 2 exact")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle timing sample (0: skip)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="independent calls per step (e.g. the layers of one chunk step), run in one batched "
+                         "launch (jb_attn_fwd_batch) when above 1")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="only run a device copy of this many MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -139,27 +142,45 @@ def main():
 
     kf = kvq.KvqFormat.make(w.bits, w.k_granularity, w.group, True, "key")
     vf = kvq.KvqFormat.make(w.bits, "token", w.group, True, "value")
-    q, kr, vr = dev(x["q"]), dev(x["k_cur"]), dev(x["v_cur"])
-    kwin = kvq.pack_window(dev(x["k_cache"]), w.chunk_len, kf)
-    vwin = kvq.pack_window(dev(x["v_cache"]), w.chunk_len, vf)
-    o = torch.empty((w.B, w.H, w.n_q, w.d), dtype=torch.float32, device="cuda")
-    ms = torch.empty((w.B, w.H, w.n_q), dtype=torch.float32, device="cuda")
-    mr = torch.empty_like(ms)
-    knext = kvq.alloc_window(kf, w.B, w.H, w.d, w.n_r, 1)
-    vnext = kvq.alloc_window(vf, w.B, w.H, w.d, w.n_r, 1)
-    a = kvq.make_args(q, kr, vr, kwin, vwin, w.chunk_len, w.n_chunks, kf, vf, o=o, mass_s=ms, mass_r=mr,
-                      correction=args.correction)
-    ws = kvq.attach_workspace(a)  # split-window partials when the grid is small for the device
+    if not 1 <= args.layers <= kvq.KVQ_BATCH_MAX:
+        print(f"--layers must be in 1..{kvq.KVQ_BATCH_MAX}", file=sys.stderr)
+        sys.exit(2)
+
+    def layer(xl):
+        """Device inputs, outputs and call arguments of one layer's attention call."""
+        t = {"q": dev(xl["q"]), "kr": dev(xl["k_cur"]), "vr": dev(xl["v_cur"])}
+        t["kwin"] = kvq.pack_window(dev(xl["k_cache"]), w.chunk_len, kf)
+        t["vwin"] = kvq.pack_window(dev(xl["v_cache"]), w.chunk_len, vf)
+        t["o"] = torch.empty((w.B, w.H, w.n_q, w.d), dtype=torch.float32, device="cuda")
+        t["ms"] = torch.empty((w.B, w.H, w.n_q), dtype=torch.float32, device="cuda")
+        t["mr"] = torch.empty_like(t["ms"])
+        t["knext"] = kvq.alloc_window(kf, w.B, w.H, w.d, w.n_r, 1)
+        t["vnext"] = kvq.alloc_window(vf, w.B, w.H, w.d, w.n_r, 1)
+        t["args"] = kvq.make_args(t["q"], t["kr"], t["vr"], t["kwin"], t["vwin"], w.chunk_len, w.n_chunks, kf, vf,
+                                  o=t["o"], mass_s=t["ms"], mass_r=t["mr"], correction=args.correction)
+        # split-window partials when the grid is small for the device (one call); the
+        # rotated queries of per-channel keys (any call)
+        t["ws"] = kvq.attach_workspace(t["args"])
+        return t
+
+    layers = [layer(x)] + [layer(synth.draw_all(w.replace(seed=w.seed + 1000 + i))) for i in range(1, args.layers)]
+    L0 = layers[0]
+    q, kr, vr, kwin, vwin, o = L0["q"], L0["kr"], L0["vr"], L0["kwin"], L0["vwin"], L0["o"]
+    knext, vnext, a = L0["knext"], L0["vnext"], L0["args"]
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        kvq.jb_attn_fwd(a, stream)
+        if len(layers) == 1:
+            kvq.jb_attn_fwd(a, stream)
+        else:
+            kvq.jb_attn_fwd_batch([t["args"] for t in layers], stream)
         if ev is not None:
             ev[1].record(stream)
-        kvq.kvq_pack(kr, kf, 1, 0, *knext, stream)
-        kvq.kvq_pack(vr, vf, 1, 0, *vnext, stream)
+        for t in layers:
+            kvq.kvq_pack(t["kr"], kf, 1, 0, *t["knext"], stream)
+            kvq.kvq_pack(t["vr"], vf, 1, 0, *t["vnext"], stream)
         if ev is not None:
             ev[2].record(stream)
 
@@ -178,15 +199,17 @@ def main():
     pack_ms = float(np.mean([e1.elapsed_time(e2) for (_, e1, e2) in evs]))
     # algorithmic bytes of the two packs: the chunk's bf16 keys and values read once, their
     # codes, steps and zero points written once
-    pack_bytes = 2 * w.bh * w.n_r * w.d * 2 + sum(t.numel() * t.element_size() for t in (*knext, *vnext))
+    nl = len(layers)
+    pack_bytes = nl * (2 * w.bh * w.n_r * w.d * 2 + sum(t.numel() * t.element_size() for t in (*knext, *vnext)))
 
-    flops = w.flops()
-    cache_bytes = (kwin[0].numel() * 4 + kwin[1].numel() * 2 * 2 + vwin[0].numel() * 4 + vwin[1].numel() * 2 * 2)
-    # algorithmic bytes of one attention call: the cache window once, Q/K_r/V_r (bf16), O and masses (fp32)
-    algo_bytes = cache_bytes + 3 * w.bh * w.n_q * w.d * 2 + w.bh * w.n_q * (w.d + 2) * 4
+    flops = nl * w.flops()
+    cache_bytes = nl * (kwin[0].numel() * 4 + kwin[1].numel() * 2 * 2 + vwin[0].numel() * 4 + vwin[1].numel() * 2 * 2)
+    # algorithmic bytes of the step's attention: the cache windows once, Q/K_r/V_r (bf16), O and masses (fp32)
+    algo_bytes = cache_bytes + nl * (3 * w.bh * w.n_q * w.d * 2 + w.bh * w.n_q * (w.d + 2) * 4)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     value = flops / (ms_step * 1e-3) / 1e12
-    traffic = traffic_from_profile()
+    # the committed counters describe one c40 launch of this kernel source
+    traffic = traffic_from_profile() if (w.name == "c40" and nl == 1 and w.bits == 2 and args.correction == 1) else None
 
     rec = {
         "metric": METRIC,
@@ -205,7 +228,8 @@ def main():
                                f"{w.n_chunks}x{w.chunk_len} cached tokens, INT{w.bits} per-{w.k_granularity} K, "
                                f"per-token V, Hadamard, correction={CORR_NAMES[args.correction]}",
                    "B": w.B, "H": w.H, "d": w.d, "n_q": w.n_q, "n_c": w.n_c, "bits": w.bits,
-                   "parallelism": "none (1 GPU)", "split_workspace_bytes": a.workspace_bytes},
+                   "parallelism": "none (1 GPU)", "split_workspace_bytes": a.workspace_bytes, "layers": nl,
+                   "batched_launch": nl > 1},
         "attn_ms": round(attn_ms, 4),
         "cache_GBps": round(cache_bytes / (attn_ms * 1e-3) / 1e9, 2),
         "window_memory": window_memory(w),

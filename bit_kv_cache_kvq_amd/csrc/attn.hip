@@ -47,6 +47,8 @@
 //    waves of a SIMD overlap each other's matrix-core and VALU work.
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "common.h"
@@ -208,8 +210,12 @@ enum : int { kNone = 0, kCached = 1, kCurrent = 2 };
 template <int K>
 using Kind = std::integral_constant<int, K>;
 
+// One workgroup's work: workgroup wg of the n_wg a call launches (n_qblk * B * H *
+// n_split; the linear ids are dealt to the XCDs round-robin, wg % 8 being the XCD). The
+// LDS is declared here rather than passed in: the kernels address it as before.
 template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
-__global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
+__device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_wg) {
+  __shared__ Smem<D> sm;
   using SM = Smem<D>;
   constexpr int HALF = D / 2;
   constexpr int KSTEPS = D / 32;  // int8 K-steps of 32 channels
@@ -237,13 +243,12 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   static_assert(KUNITS % 64 == 0 && VGROUPS % 64 == 0 && RITEMS % 64 == 0 && VITEMS % 64 == 0, "wave-uniform split");
   static_assert(KUPT <= RIPT && VGPT <= 2 * VRPT && RIPT <= 4 && VRPT <= 2, "staging registers");
   static_assert(kVST % 64 == 0 && kVST % 4 == 0, "value staging by whole waves, one token group per lane");
-  __shared__ SM sm;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, col = lane & 31;
   int qbs, bh;
-  xcd_map(blockIdx.x, gridDim.x, p.n_qblk * p.n_split, qbs, bh);
+  xcd_map(wg, n_wg, p.n_qblk * p.n_split, qbs, bh);
   const int qb = qbs / p.n_split, sp = qbs % p.n_split;  // query block, share of the tiles
   const int qi = qb * kBM + wave * 32 + col;  // this lane's query
   const bool q_ok = qi < p.n_q;
@@ -1125,6 +1130,31 @@ __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
   }
 }
 
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
+__global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
+  attn_body<D, BITS, MASS_ONLY, PERCH, EXACT>(p, blockIdx.x, gridDim.x);
+}
+
+// Several calls in one launch: call c owns workgroups start[c] .. start[c] + grid[c] - 1.
+// Every start is a multiple of 8, so a call's workgroup wg runs on XCD wg % 8 as it would
+// alone; the few workgroups between one call's end and the next start exit at once.
+constexpr int kMaxBatch = KVQ_BATCH_MAX;
+struct BatchParams {
+  Params p[kMaxBatch];
+  int start[kMaxBatch];
+  int grid[kMaxBatch];
+  int n;
+};
+
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
+__global__ __launch_bounds__(kThreads) void jb_attn_batch_kernel(const BatchParams bp) {
+  int c = 0;
+  while (c + 1 < bp.n && (int)blockIdx.x >= bp.start[c + 1]) c++;
+  const int wg = (int)blockIdx.x - bp.start[c];
+  if (wg >= bp.grid[c]) return;
+  attn_body<D, BITS, MASS_ONLY, PERCH, EXACT>(bp.p[c], wg, bp.grid[c]);
+}
+
 int validate_attn(const jb_attn_args* a, bool mass_only) {
   if (!a) return KVQ_ERR_NULL;
   const kvq_format& kf = a->k_fmt;
@@ -1279,6 +1309,25 @@ struct AttnPlan {
 // critical path: with C compute units and one workgroup per unit at a time, a grid of g
 // workgroups over T tiles takes about ceil(g S / C) rounds of ceil(T / S) tiles. A split
 // is taken only for a gain of at least 10% (the partials cost a combine pass).
+// Shares per query block for a launch of `grid` query-block workgroups over `tiles` tiles
+// each, on `cus` compute units: the cost is the rounds of the device times the tiles of
+// the longest share; a split (partial records, a merge, a prologue per share) is taken
+// only for a predicted gain of a quarter or more.
+int choose_split(long long grid, long long tiles, int cus) {
+  auto cost = [&](long long S) { return ((grid * S + cus - 1) / cus) * ((tiles + S - 1) / S); };
+  long long best = cost(1);
+  int n_split = 1;
+  for (int S = 2; S <= 8 && S <= tiles; S++) {
+    if (grid * S > 0x7FFFFFFFLL) break;
+    const long long c = cost(S);
+    if (4 * c <= 3 * best) {
+      best = c;
+      n_split = S;
+    }
+  }
+  return n_split;
+}
+
 AttnPlan plan_attn(const jb_attn_args* a) {
   AttnPlan pl;
   pl.n_qblk = (a->n_q + kBM - 1) / kBM;
@@ -1295,23 +1344,16 @@ AttnPlan plan_attn(const jb_attn_args* a) {
   }
   const long long grid = (long long)pl.n_qblk * a->B * a->H;
   const long long tiles = (long long)a->n_chunks * (chunk_pad(a->chunk_len) / kBN) + (a->n_r + kBN - 1) / kBN;
-  auto cost = [&](long long S) { return ((grid * S + cus - 1) / cus) * ((tiles + S - 1) / S); };
-  long long best = cost(1);
-  for (int S = 2; S <= 8 && S <= tiles; S++) {
-    if (grid * S > 0x7FFFFFFFLL) break;
-    const long long c = cost(S);
-    if (10 * c <= 9 * best) {
-      best = c;
-      pl.n_split = S;
-    }
-  }
+  pl.n_split = choose_split(grid, tiles, cus);
   if (pl.n_split > 1)
     pl.part_bytes = (size_t)pl.n_split * a->B * a->H * a->n_q * (size_t)(a->d + 4) * sizeof(float);
   return pl;
 }
 
-template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT = false>
-int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
+// Kernel parameters of one call under plan pl; launches the query rotation pre-pass when
+// the plan has room for it in the workspace.
+template <int D, bool MASS_ONLY, bool PERCH>
+Params fill_params(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   Params p;
   p.B = a->B;
   p.H = a->H;
@@ -1354,6 +1396,12 @@ int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   p.o = MASS_ONLY ? nullptr : a->o;
   p.mass_s = a->mass_s;
   p.mass_r = a->mass_r;
+  return p;
+}
+
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT = false>
+int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
+  const Params p = fill_params<D, MASS_ONLY, PERCH>(a, pl, st);
   const unsigned grid = (unsigned)(pl.n_qblk * a->B * a->H * pl.n_split);
   jb_attn_kernel<D, BITS, MASS_ONLY, PERCH, EXACT><<<grid, kThreads, 0, st>>>(p);
   if (pl.n_split > 1) {
@@ -1403,8 +1451,105 @@ int dispatch(const jb_attn_args* a, void* stream) {
   return perch ? launch_attn<64, 4, MASS_ONLY, true>(a, pl, s) : launch_attn<64, 4, MASS_ONLY, false>(a, pl, s);
 }
 
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
+int launch_batch(const jb_attn_args* calls, int n, hipStream_t st) {
+  // One split count S for the whole batch, chosen as for a single call but over the
+  // workgroups of all calls: rounds of the device times the longest share. It is used
+  // only when every call's workspace holds its rotated queries and its S partials.
+  AttnPlan pl[kMaxBatch];
+  long long grid1 = 0, tiles = 0;
+  for (int c = 0; c < n; c++) {
+    const jb_attn_args* a = &calls[c];
+    pl[c] = plan_attn(a);
+    grid1 += (long long)pl[c].n_qblk * a->B * a->H;
+    tiles = std::max(tiles, (long long)a->n_chunks * (chunk_pad(a->chunk_len) / kBN) + (a->n_r + kBN - 1) / kBN);
+  }
+  int S = 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                               hipSuccess && cus > 0)
+    S = choose_split(grid1, tiles, cus);
+  else
+    (void)hipGetLastError();
+  for (int c = 0; c < n && S > 1; c++) {
+    const jb_attn_args* a = &calls[c];
+    const size_t part = (size_t)S * a->B * a->H * a->n_q * (size_t)(a->d + 4) * sizeof(float);
+    if (!a->workspace || !aligned16(a->workspace) || a->workspace_bytes < pl[c].qrot_bytes + part) S = 1;
+  }
+  BatchParams bp;
+  bp.n = n;
+  long long next = 0;
+  for (int c = 0; c < n; c++) {
+    const jb_attn_args* a = &calls[c];
+    pl[c].n_split = S;
+    pl[c].part_bytes = S > 1 ? (size_t)S * a->B * a->H * a->n_q * (size_t)(a->d + 4) * sizeof(float) : 0;
+    const size_t have = a->workspace && aligned16(a->workspace) ? a->workspace_bytes : 0;
+    if (pl[c].qrot_bytes && have < pl[c].qrot_bytes) pl[c].qrot_bytes = 0;
+    bp.p[c] = fill_params<D, MASS_ONLY, PERCH>(a, pl[c], st);
+    bp.grid[c] = (int)(pl[c].n_qblk * a->B * a->H * S);
+    bp.start[c] = (int)next;
+    next += ((long long)bp.grid[c] + 7) / 8 * 8;
+    if (next > 0x7FFFFFFFLL) return KVQ_ERR_SHAPE;
+  }
+  jb_attn_batch_kernel<D, BITS, MASS_ONLY, PERCH, EXACT><<<(unsigned)next, kThreads, 0, st>>>(bp);
+  if (S > 1) {
+    constexpr int G = MASS_ONLY ? 1 : D / 4;
+    for (int c = 0; c < n; c++) {
+      const size_t rows = (size_t)calls[c].B * calls[c].H * calls[c].n_q;
+      jb_combine_kernel<D, G, MASS_ONLY><<<(unsigned)((rows * G + 255) / 256), 256, 0, st>>>(
+          bp.p[c].part, S, rows, bp.p[c].o, bp.p[c].mass_s, bp.p[c].mass_r);
+    }
+  }
+  return launch_status();
+}
+
+template <bool MASS_ONLY>
+int dispatch_batch(const jb_attn_args* calls, int n, void* stream) {
+  if (!calls) return KVQ_ERR_NULL;
+  if (n < 1 || n > kMaxBatch) return KVQ_ERR_SHAPE;
+  const jb_attn_args& a0 = calls[0];
+  for (int c = 0; c < n; c++) {
+    const int st = validate_attn(&calls[c], MASS_ONLY);
+    if (st) return st;
+    const jb_attn_args& a = calls[c];
+    if (a.d != a0.d || a.k_fmt.bits != a0.k_fmt.bits || a.k_fmt.granularity != a0.k_fmt.granularity ||
+        (a.k_fmt.granularity == KVQ_PER_CHANNEL && a.k_fmt.group != a0.k_fmt.group) ||
+        (a.correction == JB_CORR_EXACT) != (a0.correction == JB_CORR_EXACT))
+      return KVQ_ERR_UNSUPPORTED;
+  }
+  long long total = 0;
+  for (int c = 0; c < n; c++)
+    total += ((long long)(calls[c].n_q + kBM - 1) / kBM * calls[c].B * calls[c].H * 8 + 7) / 8 * 8;
+  if (total > 0x7FFFFFFFLL) return KVQ_ERR_SHAPE;  // room for up to 8 shares per call
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool perch = a0.k_fmt.granularity == KVQ_PER_CHANNEL;
+  const bool exact = a0.correction == JB_CORR_EXACT;
+#define KVQ_BATCH_CASE(D_, B_)                                                                             \
+  if (a0.d == D_ && a0.k_fmt.bits == B_) {                                                                 \
+    if (perch)                                                                                             \
+      return exact ? launch_batch<D_, B_, MASS_ONLY, true, true>(calls, n, s)                              \
+                   : launch_batch<D_, B_, MASS_ONLY, true, false>(calls, n, s);                            \
+    return exact ? launch_batch<D_, B_, MASS_ONLY, false, true>(calls, n, s)                               \
+                 : launch_batch<D_, B_, MASS_ONLY, false, false>(calls, n, s);                             \
+  }
+  KVQ_BATCH_CASE(128, 2)
+  KVQ_BATCH_CASE(128, 4)
+  KVQ_BATCH_CASE(64, 2)
+  KVQ_BATCH_CASE(64, 4)
+#undef KVQ_BATCH_CASE
+  return KVQ_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 }  // namespace kvq
+
+extern "C" int jb_attn_fwd_batch(const jb_attn_args* calls, int32_t n_calls, void* stream) {
+  return kvq::dispatch_batch<false>(calls, n_calls, stream);
+}
+
+extern "C" int jb_attn_mass_batch(const jb_attn_args* calls, int32_t n_calls, void* stream) {
+  return kvq::dispatch_batch<true>(calls, n_calls, stream);
+}
 
 extern "C" int jb_attn_fwd(const jb_attn_args* a, void* stream) { return kvq::dispatch<false>(a, stream); }
 

@@ -21,7 +21,8 @@ KVQ_ROLE_KEY, KVQ_ROLE_VALUE = 0, 1
 JB_CORR_NONE, JB_CORR_TAYLOR, JB_CORR_EXACT = 0, 1, 2
 
 EXPORTS = ("kvq_chunk_pad", "kvq_window_elems", "kvq_pack", "jb_attn_fwd", "jb_attn_mass",
-           "jb_attn_workspace_bytes", "kvq_status_str")
+           "jb_attn_fwd_batch", "jb_attn_mass_batch", "jb_attn_workspace_bytes", "kvq_status_str")
+KVQ_BATCH_MAX = 8
 
 
 class KvqError(RuntimeError):
@@ -92,6 +93,9 @@ def _load():
     lib.kvq_pack.restype = ctypes.c_int
     for fn in ("jb_attn_fwd", "jb_attn_mass"):
         getattr(lib, fn).argtypes = [ctypes.POINTER(JbAttnArgs), ctypes.c_void_p]
+        getattr(lib, fn).restype = ctypes.c_int
+    for fn in ("jb_attn_fwd_batch", "jb_attn_mass_batch"):
+        getattr(lib, fn).argtypes = [ctypes.POINTER(JbAttnArgs), ctypes.c_int32, ctypes.c_void_p]
         getattr(lib, fn).restype = ctypes.c_int
     lib.jb_attn_workspace_bytes.argtypes = [ctypes.POINTER(JbAttnArgs)]
     lib.jb_attn_workspace_bytes.restype = ctypes.c_size_t
@@ -193,6 +197,20 @@ def jb_attn_fwd(args: JbAttnArgs, stream=None):
 
 def jb_attn_mass(args: JbAttnArgs, stream=None):
     _check("jb_attn_mass", _lib.jb_attn_mass(ctypes.byref(args), _stream(stream)))
+
+
+def _batch(fn, calls, stream):
+    arr = (JbAttnArgs * len(calls))(*calls)
+    _check(fn, getattr(_lib, fn)(arr, len(calls), _stream(stream)))
+
+
+def jb_attn_fwd_batch(calls, stream=None):
+    """Several calls (a sequence of JbAttnArgs) in one launch."""
+    _batch("jb_attn_fwd_batch", calls, stream)
+
+
+def jb_attn_mass_batch(calls, stream=None):
+    _batch("jb_attn_mass_batch", calls, stream)
 
 
 def jb_attn_workspace_bytes(args: JbAttnArgs) -> int:

@@ -27,7 +27,7 @@ def kvq():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for fn in ["kvq_pack", "jb_attn_fwd", "jb_attn_mass", "jb_attn_workspace_bytes", "kvq_status_str",
-               "kvq_chunk_pad", "kvq_window_elems"]:
+               "kvq_chunk_pad", "kvq_window_elems", "jb_attn_fwd_batch", "jb_attn_mass_batch"]:
         assert fn in names
 
 
@@ -124,6 +124,34 @@ def test_attn_validation_without_launch(kvq):
     assert fwd(args(softmax_scale=-1.0)) == -2
     assert mass(args()) == -1                   # mass needs mass_s / mass_r
     assert lib.jb_attn_workspace_bytes(ctypes.byref(args())) == 0   # no device here: no split planned
+
+
+def test_batch_validation_without_launch(kvq):
+    lib = kvq._lib
+    kf = kvq.KvqFormat.make(2, "token", 128, True, "key")
+    vf = kvq.KvqFormat.make(2, "token", 128, True, "value")
+    P = 4096
+
+    def args(**kw):
+        a = kvq.JbAttnArgs(1, 1, 128, 64, 64, 64, 1, P, P, P, P, P, P, P, P, P, kf, vf, 0.0, 1, P, None, None,
+                           None, 0)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    def batch(calls, n=None):
+        arr = (kvq.JbAttnArgs * len(calls))(*calls)
+        return lib.jb_attn_fwd_batch(arr, len(calls) if n is None else n, None)
+
+    assert lib.jb_attn_fwd_batch(None, 1, None) == -1
+    assert batch([args()], n=0) == -2
+    assert batch([args()] * 9) == -2                                   # more than KVQ_BATCH_MAX
+    assert batch([args(), args(o=None)]) == -1                        # a call's own validation
+    assert batch([args(), args(d=64, k_fmt=kvq.KvqFormat.make(2, "token", 128, True, "key"))]) == -3
+    assert batch([args(), args(correction=2)]) == -3                  # exact and Taylor mixed
+    assert batch([args(), args(k_fmt=kvq.KvqFormat.make(4, "token", 128, True, "key"),
+                               v_fmt=kvq.KvqFormat.make(4, "token", 128, True, "value"))]) == -3
+    assert kvq.KVQ_BATCH_MAX == 8
 
 
 def test_sign_words(kvq):

@@ -503,3 +503,103 @@ def test_sliding_window_ring(gran):
         win.push(kr, vr)
         hist.append((x["k_cur"], x["v_cur"]))
     assert win.n_chunks == cap and win.pushed == T
+
+
+# Several calls in one launch (jb_attn_fwd_batch / jb_attn_mass_batch): shapes, windows,
+# rotations, scales and correction modes differ between the calls. Per-token calls must
+# equal the same calls run alone and unsplit bit for bit (the same workgroups compute
+# them); every call is also checked against the oracle.
+def _prepare(x, w, *, correction=1, scale=0.0, k_signs=(), v_signs=(), mass_only=False):
+    kvq = _kvq()
+    kf, vf = lib_formats(w, k_signs=k_signs, v_signs=v_signs)
+    q, kr, vr = dev(x["q"]), dev(x["k_cur"]), dev(x["v_cur"])
+    kwin = kvq.pack_window(dev(x["k_cache"]), w.chunk_len, kf) if w.n_chunks else None
+    vwin = kvq.pack_window(dev(x["v_cache"]), w.chunk_len, vf) if w.n_chunks else None
+    B, H, n_q, d = x["q"].shape
+    o = torch.full((B, H, n_q, d), float("nan"), dtype=torch.float32, device="cuda")
+    ms = torch.full((B, H, n_q), float("nan"), dtype=torch.float32, device="cuda")
+    mr = torch.full((B, H, n_q), float("nan"), dtype=torch.float32, device="cuda")
+    a = kvq.make_args(q, kr if w.n_r else None, vr if w.n_r else None, kwin, vwin, w.chunk_len, w.n_chunks, kf, vf,
+                      o=o, mass_s=ms, mass_r=mr, correction=correction, softmax_scale=scale)
+    keep = (q, kr, vr, kwin, vwin)
+    return a, (o, ms, mr), keep
+
+
+BATCH_SHAPES = [
+    (dict(B=1, H=3, d=128, n_q=300, chunk_len=200, n_chunks=2), dict(correction=1)),
+    (dict(B=2, H=1, d=128, n_q=40, chunk_len=64, n_chunks=5), dict(correction=0, scale=0.1)),
+    (dict(B=1, H=2, d=128, n_q=520, chunk_len=130, n_chunks=0), dict(correction=1)),
+    (dict(B=1, H=1, d=128, n_q=257, chunk_len=90, n_chunks=3), dict(correction=1, signs=True)),
+]
+
+
+@pytest.mark.parametrize("gran", ["token", "channel"])
+def test_batched_calls(gran):
+    kvq = _kvq()
+    calls, outs, keep, specs = [], [], [], []
+    for i, (shape, opt) in enumerate(BATCH_SHAPES):
+        w = synth.Workload("batch", **shape, k_granularity=gran, group=64,
+                           k_dist="t3" if gran == "channel" else "outlier", seed=30 + i)
+        x = synth.draw_all(w)
+        sg = dict(k_signs=synth.draw_signs(w.d, i, "k"), v_signs=synth.draw_signs(w.d, i, "v")) if opt.get("signs") \
+            else {}
+        a, out, kp = _prepare(x, w, correction=opt["correction"], scale=opt.get("scale", 0.0), **sg)
+        calls.append(a)
+        outs.append(out)
+        keep.append(kp)
+        specs.append((w, x, opt, sg))
+    print(f"attn batch {gran}: {len(calls)} calls in one launch", flush=True)
+    kvq.jb_attn_fwd_batch(calls)
+    torch.cuda.synchronize()
+    for (w, x, opt, sg), (o, ms, mr) in zip(specs, outs):
+        O, PS, PR = o.cpu().numpy(), ms.cpu().numpy(), mr.cpu().numpy()
+        Or, PSr, PRr = run_oracle(x, w, correction=CORR[opt["correction"]], scale=opt.get("scale") or None, **sg)
+        assert_attention_close(O, Or, f"batch {gran} {w.B}x{w.H}x{w.n_q}")
+        assert_mass_close(PS, PR, PSr, PRr, f"batch {gran} {w.B}x{w.H}x{w.n_q}")
+        if gran == "token":
+            O1, PS1, PR1 = run_gpu(x, w, correction=opt["correction"], scale=opt.get("scale", 0.0), split=False, **sg)
+            np.testing.assert_array_equal(O, O1)
+            np.testing.assert_array_equal(PS, PS1)
+
+
+def test_batched_calls_with_workspaces_split_together():
+    # four small calls whose workgroups leave most of the device idle: with workspaces
+    # the batch splits every call's tiles into shares and merges them per call
+    kvq = _kvq()
+    calls, outs, keep, specs, wss = [], [], [], [], []
+    for i in range(4):
+        w = synth.Workload("batchs", B=1, H=3, d=128, n_q=200 + 37 * i, chunk_len=300, n_chunks=3, seed=50 + i)
+        x = synth.draw_all(w)
+        a, out, kp = _prepare(x, w)
+        wss.append(kvq.attach_workspace(a))
+        calls.append(a)
+        outs.append(out)
+        keep.append(kp)
+        specs.append((w, x))
+    assert all(ws is not None for ws in wss), "expected a split plan for these shapes"
+    print("attn batch with workspaces (split)", flush=True)
+    kvq.jb_attn_fwd_batch(calls)
+    torch.cuda.synchronize()
+    for (w, x), (o, ms, mr) in zip(specs, outs):
+        Or, PSr, PRr = run_oracle(x, w)
+        assert_attention_close(o.cpu().numpy(), Or, f"batch split {w.n_q}")
+        assert_mass_close(ms.cpu().numpy(), mr.cpu().numpy(), PSr, PRr, f"batch split {w.n_q}")
+
+
+def test_batched_mass_only():
+    kvq = _kvq()
+    calls, outs, keep, specs = [], [], [], []
+    for i, (shape, opt) in enumerate(BATCH_SHAPES[:3]):
+        w = synth.Workload("batchm", **shape, seed=40 + i)
+        x = synth.draw_all(w)
+        a, out, kp = _prepare(x, w, correction=opt["correction"], scale=opt.get("scale", 0.0))
+        calls.append(a)
+        outs.append(out)
+        keep.append(kp)
+        specs.append((w, x, opt))
+    print("attn batch: masses only", flush=True)
+    kvq.jb_attn_mass_batch(calls)
+    torch.cuda.synchronize()
+    for (w, x, opt), (o, ms, mr) in zip(specs, outs):
+        _, PSr, PRr = run_oracle(x, w, correction=CORR[opt["correction"]], scale=opt.get("scale") or None)
+        assert_mass_close(ms.cpu().numpy(), mr.cpu().numpy(), PSr, PRr, f"batch mass {w.B}x{w.H}x{w.n_q}")

@@ -102,6 +102,11 @@ def main():
     ap.add_argument("--correction", type=int, default=1, choices=sorted(CORR_NAMES),
                     help="0 none, 1 second-order Taylor (the headline), 2 exact")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle timing sample (0: skip)")
+    ap.add_argument("--nq", type=int, default=0,
+                    help="queries (and current-chunk tokens) per head instead of the workload's; at most 32 "
+                         "takes the few-query (decode) path, whose roofline is the HBM stream of the window")
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="run without a workspace (no split, no decode path): the main kernel alone")
     ap.add_argument("--layers", type=int, default=1,
                     help="independent calls per step (e.g. the layers of one chunk step), run in one batched "
                          "launch (jb_attn_fwd_batch) when above 1")
@@ -133,6 +138,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.bits:
         w = w.replace(bits=args.bits)
+    if args.nq:
+        w = w.replace(n_q=args.nq)
     t_gen = time.perf_counter()
     x = synth.draw_all(w)
     print(f"# generated {w.name} inputs in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
@@ -160,7 +167,7 @@ def main():
                                   o=t["o"], mass_s=t["ms"], mass_r=t["mr"], correction=args.correction)
         # split-window partials when the grid is small for the device (one call); the
         # rotated queries of per-channel keys (any call)
-        t["ws"] = kvq.attach_workspace(t["args"])
+        t["ws"] = None if args.no_workspace else kvq.attach_workspace(t["args"])
         return t
 
     layers = [layer(x)] + [layer(synth.draw_all(w.replace(seed=w.seed + 1000 + i))) for i in range(1, args.layers)]
@@ -207,9 +214,12 @@ def main():
     # algorithmic bytes of the step's attention: the cache windows once, Q/K_r/V_r (bf16), O and masses (fp32)
     algo_bytes = cache_bytes + nl * (3 * w.bh * w.n_q * w.d * 2 + w.bh * w.n_q * (w.d + 2) * 4)
     achieved = flops / (attn_ms * 1e-3) / 1e12
+    decode = (w.n_q <= 32 and w.k_granularity == "token" and args.correction != 2 and a.workspace_bytes > 0
+              and nl == 1)
     value = flops / (ms_step * 1e-3) / 1e12
     # the committed counters describe one c40 launch of this kernel source
-    traffic = traffic_from_profile() if (w.name == "c40" and nl == 1 and w.bits == 2 and args.correction == 1) else None
+    traffic = traffic_from_profile() if (w.name == "c40" and nl == 1 and w.bits == 2 and args.correction == 1
+                                         and not args.nq and not args.no_workspace) else None
 
     rec = {
         "metric": METRIC,
@@ -237,10 +247,13 @@ def main():
         "pack": {"ms": round(pack_ms, 4), "algorithmic_bytes": pack_bytes,
                  "GBps": round(pack_bytes / (pack_ms * 1e-3) / 1e9, 1),
                  "frac_hbm": round(pack_bytes / (pack_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": (round(traffic) if traffic is not None else None),
-                     "algorithmic_bytes": algo_bytes, "kernel_source_sha256_16": kernel_source_hash()},
+        "roofline": ({"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(achieved / PEAK_MFMA_TFLOPS, 4)} if not decode else
+                     {"bound": "hbm", "achieved": round(algo_bytes / (attn_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": round(algo_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+        | {"traffic": (round(traffic) if traffic is not None else None),
+           "algorithmic_bytes": algo_bytes, "kernel_source_sha256_16": kernel_source_hash()},
+        "path": "decode" if decode else ("batched" if nl > 1 else "main"),
     }
     if args.cpu_heads > 0:
         heads = [(0, h) for h in range(min(args.cpu_heads, w.bh))] if w.B == 1 else \

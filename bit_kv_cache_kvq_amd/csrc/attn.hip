@@ -1155,6 +1155,421 @@ __global__ __launch_bounds__(kThreads) void jb_attn_batch_kernel(const BatchPara
   attn_body<D, BITS, MASS_ONLY, PERCH, EXACT>(bp.p[c], wg, bp.grid[c]);
 }
 
+// ---------------- few queries: one wave per share of a head's cached tiles ----------------
+// With at most 32 queries (one 32-query stream) the main kernel would keep one of its eight
+// waves busy per workgroup while the cache stream is the real cost. Here a workgroup is a
+// single wave that owns a contiguous share of one head's cached tiles and reads its
+// operands straight from global memory in MFMA order: each lane loads its own key's code
+// row half and step / zero point (the key of its M row), and the 64 cached tokens of its
+// value channels, dequantized in registers. Small per-wave LDS tables broadcast the per-key
+// factors of the logits and the value zero-point / step pairs. Queries, bias MFMA, softmax
+// and PV follow the main kernel. A share ends with its partial record (un-rotated sum,
+// reference max, l_S); the current chunk is one more share, and jb_combine_kernel merges.
+struct SmemDec {
+  float dka[kBN];        // Delta_j A, M-row order
+  uint32_t zv[kBN / 2];  // value (-1024 - z) fp16 pairs, token pair (j, j+8) order
+  uint32_t dv[kBN / 2];  // value step pairs
+};
+
+// n 32-bit words from a raw buffer at byte offset off (n = 2, 4 or 8)
+template <int N>
+__device__ inline void load_words(const __amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff, uint32_t* w) {
+  if constexpr (N == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, soff, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 4; i++) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * i, soff, 0);
+      w[4 * i] = v[0];
+      w[4 * i + 1] = v[1];
+      w[4 * i + 2] = v[2];
+      w[4 * i + 3] = v[3];
+    }
+  }
+}
+
+template <int D, int BITS, bool MASS_ONLY>
+__global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const int shares) {
+  constexpr int HALF = D / 2;
+  constexpr int KSTEPS = D / 32;
+  constexpr int CBLK = D / 32;
+  constexpr int KW = D * BITS / 32;     // key words per token
+  constexpr int KWH = KW / 2;           // key words of one half row (a lane's operand)
+  constexpr int CPW = 32 / BITS;
+  constexpr int VWPC = kBN / CPW;       // value words per channel per tile
+  constexpr int VWT = D * VWPC;         // value words per tile
+  __shared__ SmemDec sm;
+  const int lane = threadIdx.x;
+  const int h = lane >> 5, col = lane & 31;
+  const int bh = blockIdx.x / shares, sp = blockIdx.x % shares;
+  const bool q_ok = col < p.n_q;
+  const int qi = q_ok ? col : 0;
+  const float scale_l2 = p.s * kLog2e;
+
+  // ---- query operands: rotated query as 16-bit fixed point, int8 hi/lo (main kernel's build)
+  i32x4 qhi[KSTEPS], qlo[KSTEPS];
+  f16x8 qbias;
+  float A;
+  {
+    float qv[HALF];
+    const uint16_t* qrow = p.q + ((size_t)bh * p.n_q + qi) * D + HALF * h;
+    uint32_t sgw[HALF / 32];
+#pragma unroll
+    for (int k = 0; k < HALF / 32; k++) sgw[k] = h ? p.k_sg[HALF / 32 + k] : p.k_sg[k];
+#pragma unroll
+    for (int u = 0; u < HALF / 8; u++) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (q_ok) w = reinterpret_cast<const uint4*>(qrow)[u];
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int j = 8 * u + 2 * e;
+        const uint32_t we = ww[e] ^ pair_sign_xor(sgw[j >> 5], j & 31);
+        qv[j] = __uint_as_float(we << 16);
+        qv[j + 1] = __uint_as_float(we & 0xFFFF0000u);
+      }
+    }
+    if (p.k_had) {
+#pragma unroll
+      for (int hh = 1; hh < HALF; hh <<= 1)
+#pragma unroll
+        for (int i = 0; i < HALF; i++)
+          if ((i & hh) == 0) {
+            const float a = qv[i], b = qv[i + hh];
+            qv[i] = a + b;
+            qv[i + hh] = a - b;
+          }
+      const float c = rsqrtf((float)D);
+#pragma unroll
+      for (int i = 0; i < HALF; i++) {
+        const float pv = xor32(qv[i]);
+        qv[i] = (h ? (pv - qv[i]) : (qv[i] + pv)) * c;
+      }
+    }
+    float ss = 0.f, mxa = 0.f;
+#pragma unroll
+    for (int i = 0; i < HALF; i++) {
+      ss += qv[i] * qv[i];
+      mxa = fmaxf(mxa, fabsf(qv[i]));
+    }
+    ss += xor32(ss);
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));
+    const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
+    A = mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
+    int qs = 0;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; kk++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        uint32_t whi = 0, wlo = 0;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const int qf = (int)__builtin_rintf(qv[16 * kk + kperm<BITS>(j, b)] * inv);
+          const int hi = (qf + 128) >> 8;
+          const int lo = qf - (hi << 8);
+          qs += qf;
+          whi |= (uint32_t)(hi & 0xFF) << (8 * b);
+          wlo |= (uint32_t)(lo & 0xFF) << (8 * b);
+        }
+        qhi[kk][j] = (int)whi;
+        qlo[kk][j] = (int)wlo;
+      }
+    qs += __shfl_xor(qs, 32);
+    const float G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
+    _Float16 wh, wl, gh, gl;
+    split16(-A * (float)qs, wh, wl);
+    split16(-G * kD2Scale, gh, gl);
+    if (h == 0) {
+      qbias[0] = wh;
+      qbias[1] = wl;
+      qbias[2] = wh;
+      qbias[3] = gh;
+      qbias[4] = gl;
+      qbias[5] = gh;
+      qbias[6] = (_Float16)0.f;
+      qbias[7] = (_Float16)0.f;
+    } else {
+      qbias[0] = (_Float16)0.f;  // -m (hi, lo) once m is set
+      qbias[1] = (_Float16)0.f;
+      qbias[2] = (_Float16)(-kMaskLogit);
+#pragma unroll
+      for (int e = 3; e < 8; e++) qbias[e] = (_Float16)0.f;
+    }
+  }
+  float m_run = -INFINITY;
+  auto set_m = [&](float mx) KVQ_INLINE {
+    _Float16 mh, ml;
+    split16(-mx, mh, ml);
+    m_run = -((float)mh + (float)ml);
+    qbias[0] = h ? mh : qbias[0];
+    qbias[1] = h ? ml : qbias[1];
+  };
+
+  // ---- this share's cached tiles
+  const int tpc = p.cp / kBN;
+  const int n_ct = p.n_chunks * tpc;
+  const int t_beg = (int)((long long)sp * n_ct / shares), t_end = (int)((long long)(sp + 1) * n_ct / shares);
+  const size_t n_tot = (size_t)p.n_chunks * p.cp;
+  const size_t n_str = (size_t)p.n_wchunks * p.cp;
+  const __amdgpu_buffer_rsrc_t rs_kc = buffer_rsrc(p.k_codes + (size_t)bh * n_str * KW, (uint32_t)(n_tot * KW * 4));
+  const __amdgpu_buffer_rsrc_t rs_vc =
+      buffer_rsrc(p.v_codes + (size_t)bh * (n_str / kBN) * VWT, (uint32_t)(n_tot / kBN * VWT * 4));
+  const __amdgpu_buffer_rsrc_t rs_ks = buffer_rsrc(p.k_scale + (size_t)bh * n_str, (uint32_t)(n_tot * 2));
+  const __amdgpu_buffer_rsrc_t rs_kz = buffer_rsrc(p.k_zero + (size_t)bh * n_str, (uint32_t)(n_tot * 2));
+  const __amdgpu_buffer_rsrc_t rs_vs = buffer_rsrc(p.v_scale + (size_t)bh * n_str, (uint32_t)(n_tot * 2));
+  const __amdgpu_buffer_rsrc_t rs_vz = buffer_rsrc(p.v_zero + (size_t)bh * n_str, (uint32_t)(n_tot * 2));
+
+  // raw operands of one tile: this lane's key (M row col) of both blocks, its step and
+  // zero point, the value zero-point / step pair of token pair (lane), and the value
+  // words of channels 32c + col
+  struct Raw {
+    uint32_t k[2][KWH];
+    uint32_t kd[2], kz[2];
+    uint32_t vz0, vz1, vd0, vd1;
+    uint32_t v[CBLK][VWPC];
+  };
+  const int krow[2] = {mrow_key(col), 32 + mrow_key(col)};
+  const int vg = (lane >> 3) & 3, vj = lane & 7;  // value token pair (16 vg + vj, + 8)
+  auto load_raw = [&](int U, Raw& r) KVQ_INLINE {
+    const uint32_t tok0 = (uint32_t)U * kBN;
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++) {
+      load_words<KWH>(rs_kc, ((uint32_t)krow[mb] * KW + (uint32_t)h * KWH) * 4u, tok0 * KW * 4u, r.k[mb]);
+      r.kd[mb] = __builtin_amdgcn_raw_buffer_load_b16(rs_ks, (uint32_t)krow[mb] * 2u, tok0 * 2u, 0);
+      r.kz[mb] = __builtin_amdgcn_raw_buffer_load_b16(rs_kz, (uint32_t)krow[mb] * 2u, tok0 * 2u, 0);
+    }
+    if constexpr (!MASS_ONLY) {
+      const uint32_t t = (uint32_t)(16 * vg + vj);
+      r.vz0 = __builtin_amdgcn_raw_buffer_load_b16(rs_vz, t * 2u, tok0 * 2u, 0);
+      r.vz1 = __builtin_amdgcn_raw_buffer_load_b16(rs_vz, t * 2u + 16u, tok0 * 2u, 0);
+      r.vd0 = __builtin_amdgcn_raw_buffer_load_b16(rs_vs, t * 2u, tok0 * 2u, 0);
+      r.vd1 = __builtin_amdgcn_raw_buffer_load_b16(rs_vs, t * 2u + 16u, tok0 * 2u, 0);
+#pragma unroll
+      for (int c = 0; c < CBLK; c++)
+        load_words<VWPC>(rs_vc, (uint32_t)(32 * c + col) * VWPC * 4u, (uint32_t)U * VWT * 4u, r.v[c]);
+    }
+  };
+
+  float l_s = 0.f;
+  f32x16 acc[CBLK];
+#pragma unroll
+  for (int c = 0; c < CBLK; c++) acc[c] = f32x16{};
+  uint32_t pb[2][4];
+
+  // two waves per SIMD (at most 256 registers) hide each other's load latency; holding a
+  // second tile's operands in registers would cost that occupancy
+  for (int U = t_beg; U < t_end; U++) {
+    Raw cur;
+    load_raw(U, cur);
+    const int nv = min(kBN, p.chunk_len - (U % tpc) * kBN);
+    // per-key factors of both blocks into the wave's tables
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++) {
+      if (h == 0) sm.dka[32 * mb + col] = krow[mb] < nv ? half_bits_to_f32(cur.kd[mb]) * A : 0.f;
+    }
+    if constexpr (!MASS_ONLY) {
+      if (lane < kBN / 2) {
+        const bool ok0 = 16 * vg + vj < nv, ok1 = 16 * vg + vj + 8 < nv;
+        sm.zv[lane] = pack_f16x2(ok0 ? -1024.f - half_bits_to_f32(cur.vz0) : -1024.f,
+                                 ok1 ? -1024.f - half_bits_to_f32(cur.vz1) : -1024.f);
+        sm.dv[lane] = (ok0 ? (cur.vd0 & 0xFFFFu) : 0u) | ((ok1 ? (cur.vd1 & 0xFFFFu) : 0u) << 16);
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++) {
+      // bias operand of this lane's M row: slots 0..7 (h = 0) or 8..15 (h = 1)
+      uint4 kbop = make_uint4(0, 0, 0, 0);
+      const bool kv = krow[mb] < nv;
+      if (h == 0) {
+        if (kv) {
+          const float dk = half_bits_to_f32(cur.kd[mb]), zk = half_bits_to_f32(cur.kz[mb]);
+          _Float16 dzh, dzl, d2h, d2l;
+          split16(dk * zk, dzh, dzl);
+          split16(dk * dk * (1.f / kD2Scale), d2h, d2l);
+          const uint32_t dzh_b = __builtin_bit_cast(uint16_t, dzh), dzl_b = __builtin_bit_cast(uint16_t, dzl);
+          const uint32_t d2h_b = __builtin_bit_cast(uint16_t, d2h), d2l_b = __builtin_bit_cast(uint16_t, d2l);
+          kbop = make_uint4(dzh_b | (dzh_b << 16), dzl_b | (d2h_b << 16), d2h_b | (d2l_b << 16), 0u);
+        }
+      } else {
+        const uint32_t one = 0x3C00u;
+        kbop = make_uint4(one | (one << 16), kv ? 0u : one, 0u, 0u);
+      }
+      // key codes as int8 (kperm order in each 16-channel unit)
+      i32x4 kop[KSTEPS];
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; kk++) {
+        if constexpr (BITS == 2) {
+          const uint32_t w = cur.k[mb][kk];
+          kop[kk] = i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
+                          (int)((w >> 6) & 0x03030303u)};
+        } else {
+          const uint32_t w0 = cur.k[mb][2 * kk], w1 = cur.k[mb][2 * kk + 1];
+          kop[kk] = i32x4{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+                          (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+        }
+      }
+      const f32x16 zf = {};
+      const f32x16 cbv = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kbop), qbias, zf, 0, 0, 0);
+      i32x16 sq = {};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; kk++) sq = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[kk], qhi[kk], sq, 0, 0, 0);
+      sq = sq << 8;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; kk++) sq = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[kk], qlo[kk], sq, 0, 0, 0);
+      // logits (log2 units, -m through the bias) and softmax numerators
+      float x[16];
+#pragma unroll
+      for (int v4 = 0; v4 < 4; v4++) {
+        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dka[32 * mb + 8 * v4 + 4 * h]);
+        const float d[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int b = 0; b < 4; b++) x[4 * v4 + b] = fmaf(d[b], (float)sq[4 * v4 + b], cbv[4 * v4 + b]);
+      }
+      auto pairs = [&](float off) KVQ_INLINE {
+        float ls2[2] = {0.f, 0.f};
+        const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+        for (int v2 = 0; v2 < 8; v2++) {
+          const uint32_t pr = pack_f16x2(exp2_(x[2 * v2] - off), exp2_(x[2 * v2 + 1] - off));
+          pb[v2 >> 2][v2 & 3] = pr;
+          ls2[v2 & 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pr), ones, ls2[v2 & 1], false);
+        }
+        return ls2[0] + ls2[1];
+      };
+      float lsum;
+      if (__builtin_amdgcn_readfirstlane(m_run == -INFINITY ? 1 : 0)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; v++) mx = fmaxf(mx, x[v]);
+        mx = fmaxf(mx, xor32(mx));
+        set_m(mx + kHeadroom);
+        lsum = pairs(m_run);
+      } else {
+        lsum = pairs(0.f);
+        const bool raise = !(lsum <= kPmax);
+        if (__ballot(raise) != 0) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 16; v++) mx = fmaxf(mx, x[v]);
+          mx = fmaxf(mx, xor32(mx));
+          const float partner_raise = xor32(raise ? 1.f : 0.f);
+          const bool up = raise || partner_raise != 0.f;
+          const float m_old = m_run;
+          set_m(up ? m_old + mx : m_old);
+          const float sc = exp2_(m_old - m_run);
+          l_s *= sc;
+          if constexpr (!MASS_ONLY) {
+#pragma unroll
+            for (int c = 0; c < CBLK; c++)
+#pragma unroll
+              for (int v = 0; v < 16; v++) acc[c][v] *= sc;
+          }
+          lsum = pairs(m_run - m_old);
+        }
+      }
+      l_s += lsum;
+      if constexpr (!MASS_ONLY) {
+        // value operands: fp16((code - z) Delta) of positions 16 ks + 8 h .. + 7 (token
+        // pairs (j, j + 8), j = 4 h .. 4 h + 3, of 16-token group 2 mb + ks)
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+          const int g = 2 * mb + ks;
+          const uint4 z4 = *reinterpret_cast<const uint4*>(&sm.zv[8 * g + 4 * h]);
+          const uint4 d4 = *reinterpret_cast<const uint4*>(&sm.dv[8 * g + 4 * h]);
+          const uint32_t zz[4] = {z4.x, z4.y, z4.z, z4.w}, dd[4] = {d4.x, d4.y, d4.z, d4.w};
+          f16x8 vop[CBLK];
+#pragma unroll
+          for (int c = 0; c < CBLK; c++) {
+            uint32_t t;
+            if constexpr (BITS == 2) {
+              t = (cur.v[c][g] >> (8 * h)) & 0x00FF00FFu;
+            } else {
+              const uint32_t w0 = cur.v[c][2 * g], w1 = cur.v[c][2 * g + 1];
+              t = h ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
+            }
+            uint32_t res[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const uint32_t a = BITS == 2 ? (((t >> (2 * i)) & 0x00030003u) | 0x64006400u)
+                                           : (((t >> (4 * i)) & 0x000F000Fu) | 0x64006400u);
+              const f16x2 cz = __builtin_bit_cast(f16x2, a) + __builtin_bit_cast(f16x2, zz[i]);
+              res[i] = __builtin_bit_cast(uint32_t, cz * __builtin_bit_cast(f16x2, dd[i]));
+            }
+            vop[c] = __builtin_bit_cast(f16x8, make_uint4(res[0], res[1], res[2], res[3]));
+          }
+          const f16x8 bop = __builtin_bit_cast(f16x8, make_uint4(pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]));
+#pragma unroll
+          for (int c = 0; c < CBLK; c++) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[c], bop, acc[c], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- un-rotate the value sum (as the main kernel) and write the share's partial record
+  if constexpr (!MASS_ONLY) {
+    if (p.v_had) {
+#pragma unroll
+      for (int bit = 0; bit < 4; bit++)
+#pragma unroll
+        for (int c = 0; c < CBLK; c++)
+#pragma unroll
+          for (int v = 0; v < 16; v++)
+            if ((v & (1 << bit)) == 0) {
+              const float a = acc[c][v], b = acc[c][v | (1 << bit)];
+              acc[c][v] = a + b;
+              acc[c][v | (1 << bit)] = a - b;
+            }
+#pragma unroll
+      for (int c = 0; c < CBLK; c++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const float pvv = xor32(acc[c][v]);
+          acc[c][v] = h ? (pvv - acc[c][v]) : (acc[c][v] + pvv);
+        }
+#pragma unroll
+      for (int cbk = 1; cbk < CBLK; cbk <<= 1)
+#pragma unroll
+        for (int c = 0; c < CBLK; c++)
+          if ((c & cbk) == 0)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+              const float a = acc[c][v], b = acc[c | cbk][v];
+              acc[c][v] = a + b;
+              acc[c | cbk][v] = a - b;
+            }
+      const float cn = rsqrtf((float)D);
+#pragma unroll
+      for (int c = 0; c < CBLK; c++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[c][v] *= cn;
+      if (p.v_sg[0] | p.v_sg[1] | p.v_sg[2] | p.v_sg[3]) {
+#pragma unroll
+        for (int c = 0; c < CBLK; c++) {
+          const uint32_t wv = p.v_sg[c] >> (4 * h);
+#pragma unroll
+          for (int v = 0; v < 16; v++)
+            acc[c][v] = __uint_as_float(__float_as_uint(acc[c][v]) ^ (((wv >> ((v & 3) + 8 * (v >> 2))) & 1u) << 31));
+        }
+      }
+    }
+  }
+  const float ls = l_s + xor32(l_s);
+  if (!q_ok) return;
+  float* rec = p.part + (((size_t)sp * p.B * p.H + bh) * p.n_q + qi) * (D + 4);
+  if constexpr (!MASS_ONLY) {
+#pragma unroll
+    for (int c = 0; c < CBLK; c++)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; v4++)
+        *reinterpret_cast<float4*>(rec + 32 * c + 8 * v4 + 4 * h) =
+            make_float4(acc[c][4 * v4], acc[c][4 * v4 + 1], acc[c][4 * v4 + 2], acc[c][4 * v4 + 3]);
+  }
+  if (h == 0) *reinterpret_cast<float4*>(rec + D) = make_float4(m_run, ls, 0.f, 0.f);
+}
+
 int validate_attn(const jb_attn_args* a, bool mass_only) {
   if (!a) return KVQ_ERR_NULL;
   const kvq_format& kf = a->k_fmt;
@@ -1303,6 +1718,8 @@ struct AttnPlan {
   int n_qblk, n_split;
   size_t part_bytes;  // workspace the split needs (0 for n_split == 1)
   size_t qrot_bytes;  // workspace of the rotated queries (per-channel rotated keys), else 0
+  int dec_shares;     // few queries: shares of the cached tiles per head (0: no decode path)
+  size_t dec_bytes;   // workspace of the decode path's partial records
 };
 
 // Splits each query block's tile sequence over n_split workgroups when that shortens the
@@ -1336,11 +1753,24 @@ AttnPlan plan_attn(const jb_attn_args* a) {
   pl.qrot_bytes = (a->k_fmt.granularity == KVQ_PER_CHANNEL && a->k_fmt.hadamard && a->n_chunks > 0)
                       ? (size_t)a->B * a->H * a->n_q * (size_t)a->d * sizeof(float)
                       : 0;
+  pl.dec_shares = 0;
+  pl.dec_bytes = 0;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 1) {
     (void)hipGetLastError();
     return pl;
+  }
+  // At most 32 queries (one stream) with per-token keys and a cached window: the decode
+  // path, with as many one-wave shares as fit on the device at once (two per SIMD)
+  const long long n_ct = (long long)a->n_chunks * (chunk_pad(a->chunk_len) / kBN);
+  if (a->n_q <= 32 && a->k_fmt.granularity == KVQ_PER_TOKEN && a->correction != JB_CORR_EXACT && n_ct > 0) {
+    const long long bhc = (long long)a->B * a->H;
+    const long long S = std::min(n_ct, std::max(1LL, 8LL * cus / bhc));
+    if (S * bhc <= 0x7FFFFFFFLL) {
+      pl.dec_shares = (int)S;
+      pl.dec_bytes = (size_t)(S + (a->n_r > 0 ? 1 : 0)) * bhc * a->n_q * (size_t)(a->d + 4) * sizeof(float);
+    }
   }
   const long long grid = (long long)pl.n_qblk * a->B * a->H;
   const long long tiles = (long long)a->n_chunks * (chunk_pad(a->chunk_len) / kBN) + (a->n_r + kBN - 1) / kBN;
@@ -1413,14 +1843,51 @@ int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   return launch_status();
 }
 
+// Few queries: the decode kernel over the cached window (one partial record per share),
+// the main kernel over the current chunk as one more partial record, then the merge.
+template <int D, int BITS, bool MASS_ONLY>
+int launch_decode(const jb_attn_args* a, const AttnPlan& pl0, hipStream_t st) {
+  AttnPlan pl = pl0;
+  pl.n_split = 1;
+  pl.qrot_bytes = 0;
+  pl.part_bytes = 0;
+  Params p = fill_params<D, MASS_ONLY, false>(a, pl, st);
+  const int S = pl.dec_shares;
+  const size_t rows = (size_t)a->B * a->H * a->n_q;
+  float* part = static_cast<float*>(a->workspace);
+  p.part = part;
+  jb_decode_kernel<D, BITS, MASS_ONLY><<<(unsigned)(S * a->B * a->H), 64, 0, st>>>(p, S);
+  int n_rec = S;
+  if (a->n_r > 0) {
+    Params pc = p;
+    pc.n_chunks = 0;
+    pc.n_wchunks = 0;
+    pc.part = part + (size_t)S * rows * (D + 4);
+    pc.n_split = 1;
+    jb_attn_kernel<D, BITS, MASS_ONLY, false, false><<<(unsigned)(pl.n_qblk * a->B * a->H), kThreads, 0, st>>>(pc);
+    n_rec++;
+  }
+  constexpr int G = MASS_ONLY ? 1 : D / 4;
+  jb_combine_kernel<D, G, MASS_ONLY><<<(unsigned)((rows * G + 255) / 256), 256, 0, st>>>(part, n_rec, rows, p.o,
+                                                                                         p.mass_s, p.mass_r);
+  return launch_status();
+}
+
 template <bool MASS_ONLY>
 int dispatch(const jb_attn_args* a, void* stream) {
   const int st = validate_attn(a, MASS_ONLY);
   if (st) return st;
   AttnPlan pl = plan_attn(a);
+  const size_t have = a->workspace ? a->workspace_bytes : 0;
+  if (pl.dec_shares && have >= pl.dec_bytes) {
+    if (!aligned16(a->workspace)) return KVQ_ERR_ALIGN;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (a->d == 128)
+      return a->k_fmt.bits == 2 ? launch_decode<128, 2, MASS_ONLY>(a, pl, s) : launch_decode<128, 4, MASS_ONLY>(a, pl, s);
+    return a->k_fmt.bits == 2 ? launch_decode<64, 2, MASS_ONLY>(a, pl, s) : launch_decode<64, 4, MASS_ONLY>(a, pl, s);
+  }
   // the workspace serves the rotated queries first, then the split partials; what does
   // not fit is done without (in-kernel rotation, an unsplit grid)
-  const size_t have = a->workspace ? a->workspace_bytes : 0;
   if (pl.qrot_bytes && have < pl.qrot_bytes) pl.qrot_bytes = 0;
   if (pl.n_split > 1 && have < pl.qrot_bytes + pl.part_bytes) {
     pl.n_split = 1;
@@ -1558,5 +2025,5 @@ extern "C" int jb_attn_mass(const jb_attn_args* a, void* stream) { return kvq::d
 extern "C" size_t jb_attn_workspace_bytes(const jb_attn_args* a) {
   if (kvq::validate_attn(a, false) != KVQ_OK && kvq::validate_attn(a, true) != KVQ_OK) return 0;
   const kvq::AttnPlan pl = kvq::plan_attn(a);
-  return pl.qrot_bytes + pl.part_bytes;
+  return pl.dec_shares ? pl.dec_bytes : pl.qrot_bytes + pl.part_bytes;
 }

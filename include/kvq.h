@@ -198,6 +198,12 @@ int jb_attn_mass(const jb_attn_args* a, void* stream);
 int jb_attn_fwd_batch(const jb_attn_args* calls, int32_t n_calls, void* stream);
 int jb_attn_mass_batch(const jb_attn_args* calls, int32_t n_calls, void* stream);
 
+/* Few queries (n_q <= 32, per-token keys, correction other than exact): with a workspace of
+ * the size jb_attn_workspace_bytes reports, the call streams each head's cached window in
+ * one-wave shares (a decode-like regime, bound by the cache stream rather than the matrix
+ * cores), computes the current chunk as one more share and merges the shares' partial
+ * records; without it, the main kernel runs unsplit. */
+
 /* Workspace bytes a call with these arguments uses on the current device (0: none).
  * When the grid of query blocks is small for the device (fewer workgroups than its compute
  * units can take in whole rounds), the call splits each query block's tiles (cached

@@ -603,3 +603,56 @@ def test_batched_mass_only():
     for (w, x, opt), (o, ms, mr) in zip(specs, outs):
         _, PSr, PRr = run_oracle(x, w, correction=CORR[opt["correction"]], scale=opt.get("scale") or None)
         assert_mass_close(ms.cpu().numpy(), mr.cpu().numpy(), PSr, PRr, f"batch mass {w.B}x{w.H}x{w.n_q}")
+
+
+# Few queries (n_q <= 32) with per-token keys: with a workspace the call runs the decode
+# path (one-wave shares of each head's cached tiles, the current chunk as one more share,
+# merged); without one, the main kernel. Both against the oracle on every row.
+DECODE_SHAPES = [
+    dict(B=1, H=3, d=128, n_q=16, chunk_len=300, n_chunks=4),
+    dict(B=2, H=2, d=128, n_q=32, chunk_len=64, n_chunks=9),
+    dict(B=1, H=2, d=64, n_q=5, chunk_len=130, n_chunks=3),
+    dict(B=1, H=1, d=128, n_q=1, chunk_len=37, n_chunks=6),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda s: "x".join(str(v) for v in s.values()))
+@pytest.mark.parametrize("bits", [2, 4])
+def test_decode_path_all_rows(shape, bits):
+    w = synth.Workload("dec", **shape, bits=bits, seed=60)
+    print(f"attn decode {shape} bits={bits}", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w, split=True)
+    assert run_gpu.last_workspace_bytes > 0, "expected the decode path"
+    O1, PS1, PR1 = run_gpu(x, w, split=False)
+    Or, PSr, PRr = run_oracle(x, w)
+    assert_attention_close(O, Or, f"decode {shape} b{bits}")
+    assert_mass_close(PS, PR, PSr, PRr, f"decode {shape} b{bits}")
+    assert_attention_close(O1, Or, f"main {shape} b{bits}")
+
+
+def test_decode_path_variants():
+    w = synth.Workload("dec", B=1, H=2, d=128, n_q=20, chunk_len=200, n_chunks=5, seed=61)
+    x = synth.draw_all(w)
+    print("attn decode: no current chunk, masses only, signs, no correction", flush=True)
+    # no current chunk: the cached shares only
+    xn = dict(x, k_cur=x["k_cur"][:, :, :0], v_cur=x["v_cur"][:, :, :0])
+    wn = w.replace(n_q=20)
+    O, PS, PR = run_gpu(xn, wn)
+    Or, PSr, PRr = run_oracle(xn, wn)
+    assert_attention_close(O, Or, "decode no current")
+    assert np.abs(PS - 1).max() <= 1e-6
+    # masses only
+    _, PS, PR = run_gpu(x, w, mass_only=True)
+    _, PSr, PRr = run_oracle(x, w)
+    assert_mass_close(PS, PR, PSr, PRr, "decode masses only")
+    # randomized rotations and no correction
+    ks, vs = synth.draw_signs(w.d, 7, "k"), synth.draw_signs(w.d, 7, "v")
+    O, PS, PR = run_gpu(x, w, correction=0, k_signs=ks, v_signs=vs)
+    Or, PSr, PRr = run_oracle(x, w, correction="none", k_signs=ks, v_signs=vs)
+    assert_attention_close(O, Or, "decode signs")
+    assert_mass_close(PS, PR, PSr, PRr, "decode signs")
+    # the exact correction takes the main kernel (no decode workspace is asked for)
+    O, PS, PR = run_gpu(x, w, correction=2)
+    Or, PSr, PRr = run_oracle(x, w, correction="exact")
+    assert_attention_close(O, Or, "decode exact")

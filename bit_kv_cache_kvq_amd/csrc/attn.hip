@@ -44,7 +44,14 @@
 //    (exact products) and fp16 PV.
 //  * Keys and per-key parameters are staged two tiles ahead, values one tile ahead
 //    (a three-slot LDS ring), by all eight waves, with one barrier per tile; the two
-//    waves of a SIMD overlap each other's matrix-core and VALU work.
+//    waves of a SIMD overlap each other's matrix-core and VALU work in part.
+//  * A grid too small for the device splits each query block's tiles into shares whose
+//    partial records a second kernel merges; several calls may share one launch; with
+//    at most 32 queries a one-wave kernel streams shares of the cached window instead
+//    (few queries: the cache stream, not the matrix cores, bounds the call).
+//  * Options: the exact correction sum_c log(sinh(x_c) / x_c), x_c = s q'_c Delta_c / 2
+//    (an ablation of the second-order form), randomized rotations H diag(s), and a
+//    window stride larger than the chunks attended (a ring of chunk slots).
 #include <math.h>
 
 #include <algorithm>

@@ -545,8 +545,9 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // ---------------- staging (all threads) ----------------
   // Step T stages the keys, per-key parameters and value zero-point / step pairs of
   // tile T+2, and the values of tile T+1. Global loads are issued at the start of the
-  // step, unconditional, with indices clamped into the arrays (positions past the end
-  // are replaced when stored); the LDS stores come at its end, before the barrier.
+  // step (per-channel keys: in the step before), unconditional, with indices clamped into
+  // the arrays (positions past the end are replaced when stored); the LDS stores come
+  // later in the step, before its barrier.
   uint4 kpre[RIPT];          // keys (code units, or current rows)
   uint4 vpre[2 * VRPT];      // values (code groups, or current row pairs)
   uint32_t pk_dk = 0, pk_zk = 0;                 // key step / zero point of key tid & 63
@@ -1015,6 +1016,11 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     }
   };
 
+  // Per-channel keys issue a tile's global loads a step earlier: its keys right after the
+  // previous tile's keys are stored, its values right after the previous values are
+  // stored (before the barrier), so the loads have a whole step to arrive; per-token keys
+  // issue both at the step start (measured faster there).
+  constexpr bool kEarlyK = PERCH;
   // Step T of a run of n_t tiles of one kind (tile index U = U0 + T in LDS slot slot0;
   // the next two tiles in slots slot1, slot2): QK^T, softmax and PV of the tile's two 32-key
   // blocks, while the keys of tile U+2 and the values of tile U+1 are staged. FIRST:
@@ -1024,8 +1030,8 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     const std::false_type no;
     const int U = U0 + T;
     const bool stage_k = T + 2 < n_t, stage_v = T + 1 < n_t;
-    if (stage_k) load_k(U + 2, k_c);
-    if (stage_v) load_v(U + 1, k_c);
+    if (!kEarlyK && stage_k) load_k(U + 2, k_c);
+    if (!kEarlyK && stage_v) load_v(U + 1, k_c);
     if (computes) {
       if constexpr (PERCH && decltype(k_c)::value == kCached) {
         if (T == 0 || (U % tiles_per_chunk) % k_tpg == 0) refresh_group(slot0);
@@ -1045,13 +1051,16 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       __builtin_amdgcn_sched_barrier(0);
       // the key staging (VALU and LDS writes) runs in the shadow of block 1's QK^T MFMAs
       if (stage_k) store_k(U + 2, slot2, k_c);
+      if (kEarlyK && T + 3 < n_t) load_k(U + 3, k_c);
       __builtin_amdgcn_sched_barrier(0);
       softmax(slot0, 1, set0, k_c, no);
       pv();
-    } else if (stage_k) {
-      store_k(U + 2, slot2, k_c);
+    } else {
+      if (stage_k) store_k(U + 2, slot2, k_c);
+      if (kEarlyK && T + 3 < n_t) load_k(U + 3, k_c);
     }
     if (stage_v) store_v(U + 1, slot1, k_c);
+    if (kEarlyK && T + 2 < n_t) load_v(U + 2, k_c);
     __syncthreads();
   };
   // All tiles of one kind (tile U0 + T in slot T mod 3, the slots rotating with T): stage
@@ -1067,6 +1076,8 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     __syncthreads();
     load_v(U0, k_c);
     store_v(U0, 0, k_c);
+    if (kEarlyK && n_t > 2) load_k(U0 + 2, k_c);
+    if (kEarlyK && n_t > 1) load_v(U0 + 1, k_c);
     __syncthreads();
     step(U0, n_t, 0, 0, 1, 2, k_c, std::true_type());
     int s0 = 1, s1 = 2, s2 = 0;

@@ -165,8 +165,8 @@ def main():
         t["vnext"] = kvq.alloc_window(vf, w.B, w.H, w.d, w.n_r, 1)
         t["args"] = kvq.make_args(t["q"], t["kr"], t["vr"], t["kwin"], t["vwin"], w.chunk_len, w.n_chunks, kf, vf,
                                   o=t["o"], mass_s=t["ms"], mass_r=t["mr"], correction=args.correction)
-        # split-window partials when the grid is small for the device (one call); the
-        # rotated queries of per-channel keys (any call)
+        # split-window partials when the grid is small for the device (one call) and the
+        # records of the few-query path
         t["ws"] = None if args.no_workspace else kvq.attach_workspace(t["args"])
         return t
 

@@ -29,7 +29,8 @@
 //  * Keys quantized per channel over token groups (Delta_gc, z_gc): at each group's
 //    first tile the wave rescales its rotated query by the group's steps, re-quantizes
 //    it (scale a_ch) and folds the group's zero-point and correction terms into a
-//    per-query constant carried by the bias MFMA; the logit is x = a_ch S + c.
+//    per-query constant carried by the bias MFMA; the logit is x = a_ch S + c. The
+//    rotated queries stay in LDS (16-bit fixed point) for the whole cached window.
 //  * The reference max m starts at the first block's maximum plus a headroom of 2^2 (a
 //    larger headroom pushes keys a few binades below the max into fp16 subnormals) and
 //    stays fixed while every p = exp2(x) fits fp16 (checked by the fp16 row sum of each
@@ -107,7 +108,6 @@ struct Params {
   int k_group;  // tokens per key channel group (per-channel keys), else 0
   int n_split;  // workgroups per query block, each over a contiguous share of the tiles
   float* part;  // n_split > 1: partial records [n_split][B*H][n_q][D + 4], else null
-  const float* qrot;  // per-channel rotated keys: H q / sqrt(d) fp32 [B*H][n_q][D], else null
   float* o;
   float* mass_s;
   float* mass_r;
@@ -187,11 +187,12 @@ __device__ inline void xcd_map(int L, int total, int n_qblk, int& qb, int& bh) {
 }
 
 template <int D>
-struct Smem {
+struct SmemSlots {
   static constexpr int VROW = kBN + 8;  // fp16 per value row (padded against bank conflicts)
   static constexpr int KROW = D + 16;   // bytes per unpacked key row
+  typedef uint8_t KCodes[kBN][KROW];    // cached key codes (kperm order per 16 channels)
   union KSlot {
-    uint8_t c[kBN][KROW];     // cached key codes (kperm order per 16 channels)
+    KCodes c;
     uint16_t kr[kBN][D + 8];  // current-chunk keys (bf16), natural order
   };
   struct PSlot {
@@ -204,11 +205,39 @@ struct Smem {
     uint32_t zv[kBN / 2];   // (-1024 - z^V) fp16 pairs, token pair (j, j+8) order
     uint32_t dvp[kBN / 2];  // (Delta^V_j, Delta^V_j+8) fp16 pairs
   };
-  alignas(16) KSlot k[3];
-  alignas(16) _Float16 v[3][D][VROW];  // value rows: fp16((code - z) Delta^V) or current values
-  alignas(16) PSlot prm[3];
-  alignas(16) ZSlot z[3];
+};
+
+// The LDS of a workgroup: a three-slot ring of key, value and parameter tiles.
+template <int D, bool PERCH = false>
+struct Smem : SmemSlots<D> {
+  using T = SmemSlots<D>;
+  alignas(16) typename T::KSlot k[3];
+  alignas(16) _Float16 v[3][D][T::VROW];  // value rows: fp16((code - z) Delta^V) or current values
+  alignas(16) typename T::PSlot prm[3];
+  alignas(16) typename T::ZSlot z[3];
   alignas(16) float a_stream[kNS];
+  __device__ typename T::KCodes& kc(int s) { return k[s].c; }
+};
+
+// Per-channel keys also keep each stream's rotated queries in LDS during the cached tiles,
+// as 16-bit fixed point (32 queries x D per wave; the 16-byte chunks of a row are swizzled
+// by the query index against bank conflicts), behind three packed code slots; the current
+// chunk's key slots overlay both.
+template <int D>
+struct Smem<D, true> : SmemSlots<D> {
+  using T = SmemSlots<D>;
+  union {
+    typename T::KSlot k[3];
+    struct {
+      typename T::KCodes c[3];
+      int16_t qf[kNS * 32 * D];
+    } pc;
+  };
+  alignas(16) _Float16 v[3][D][T::VROW];
+  alignas(16) typename T::PSlot prm[3];
+  alignas(16) typename T::ZSlot z[3];
+  alignas(16) float a_stream[kNS];
+  __device__ typename T::KCodes& kc(int s) { return pc.c[s]; }
 };
 
 #define KVQ_INLINE __attribute__((always_inline))
@@ -222,8 +251,8 @@ using Kind = std::integral_constant<int, K>;
 // LDS is declared here rather than passed in: the kernels address it as before.
 template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
 __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_wg) {
-  __shared__ Smem<D> sm;
-  using SM = Smem<D>;
+  __shared__ Smem<D, PERCH> sm;
+  using SM = Smem<D, PERCH>;
   constexpr int HALF = D / 2;
   constexpr int KSTEPS = D / 32;  // int8 K-steps of 32 channels
   constexpr int CBLK = D / 32;    // 32-channel output blocks
@@ -459,21 +488,54 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   float a_ch = 0.f;
   // The group's step and zero-point rows come from the tile's parameter slot (staged with
   // the tile's keys): D fp16 steps, then D fp16 zero points.
+  // The rotated query rows stay in LDS for the cached tiles as q'_f = rint(q' / sq0) in
+  // 16 bits (sq0 = max |q'| / 32767 per query); a refresh starts from q'_f, so the group
+  // terms below carry sq0 where they need q~ itself.
+  float sq0 = 0.f;
+  auto qf_chunk = [&](int u) KVQ_INLINE -> uint4* {  // 16-byte chunk u of this lane's half row
+    if constexpr (PERCH)
+      return reinterpret_cast<uint4*>(&sm.pc.qf[(wave * 32 + col) * D]) + (((HALF / 8) * h + u) ^ (col & 7));
+    else
+      return nullptr;
+  };
+  auto fill_qf = [&]() KVQ_INLINE {
+    float qv[HALF];
+    rotated_query(qv);
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < HALF; i++) mx = fmaxf(mx, fabsf(qv[i]));
+    mx = fmaxf(mx, xor32(mx));
+    sq0 = mx * (1.f / 32767.f);
+    const float inv = mx > 0.f ? 32767.f / mx : 0.f;
+#pragma unroll
+    for (int u = 0; u < HALF / 8; u++) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int a = (int)rintf(qv[8 * u + 2 * e] * inv), b = (int)rintf(qv[8 * u + 2 * e + 1] * inv);
+        w[e] = ((uint32_t)a & 0xFFFFu) | ((uint32_t)b << 16);
+      }
+      *qf_chunk(u) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  };
   auto refresh_group = [&](int slot) KVQ_INLINE {
     const uint4* drow = reinterpret_cast<const uint4*>(&sm.prm[slot].dka[0][0]) + HALF * h / 8;
     const uint4* zrow = drow + D / 8;
     float qv[HALF];
-    if (p.qrot) {  // rotated once for the whole call by jb_rotate_q_kernel
-      const float4* src = reinterpret_cast<const float4*>(p.qrot + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h);
+    if constexpr (PERCH) {
 #pragma unroll
-      for (int u = 0; u < HALF / 4; u++) {
-        const float4 v = src[u];
-        qv[4 * u] = v.x;
-        qv[4 * u + 1] = v.y;
-        qv[4 * u + 2] = v.z;
-        qv[4 * u + 3] = v.w;
+      for (int u = 0; u < HALF / 8; u++) {
+        const uint4 w = *qf_chunk(u);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          qv[8 * u + 2 * e] = (float)(int)(int16_t)(ww[e] & 0xFFFFu);
+          qv[8 * u + 2 * e + 1] = (float)((int)ww[e] >> 16);
+        }
       }
     } else {
+      // never called for per-token keys; the reference keeps their kernels' code unchanged
+      // (the per-token loop measured 1.5% slower when this lambda did not use it)
       rotated_query(qv);
     }
     float ss = 0.f, mxa = 0.f;
@@ -495,13 +557,13 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     float bx = 0.f;  // exact correction: sum_c log_sinhc(s q~_c / 2)
     if constexpr (EXACT) {
 #pragma unroll
-      for (int i = 0; i < HALF; i++) bx += log_sinhc(0.5f * p.s * qv[i]);
+      for (int i = 0; i < HALF; i++) bx += log_sinhc((0.5f * p.s * sq0) * qv[i]);
       bx += xor32(bx);
     }
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));  // stream-wide max
     const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
-    a_ch = mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
+    a_ch = mxa > 0.f ? scale_l2 * (mxa * sq0 / kQFix) : 0.f;
     float zs = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; kk++) {
@@ -537,7 +599,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       }
     }
     zs += xor32(zs);
-    const float G = EXACT ? bx * kLog2e : p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
+    const float G = EXACT ? bx * kLog2e : p.correction ? p.s * p.s * (sq0 * sq0) * ss * (1.f / 24.f) * kLog2e : 0.f;
     c_grp = -a_ch * zs - G;
     write_mslot();
   };
@@ -616,7 +678,10 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           const uint32_t w0 = kpre[i].x, w1 = kpre[i].y;
           lo = make_uint4(w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu);
         }
-        *reinterpret_cast<uint4*>(&ks.c[tok][16 * ui]) = lo;
+        if constexpr (PERCH)
+          *reinterpret_cast<uint4*>(&sm.kc(slot)[tok][16 * ui]) = lo;
+        else
+          *reinterpret_cast<uint4*>(&ks.c[tok][16 * ui]) = lo;
       }
       // Delta_j A of each wave's stream; 0 for padding keys (their logit is set by the mask)
       if constexpr (PERCH) {
@@ -807,7 +872,9 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     kbop = sm.prm[slot].kb[32 * mb + col][h];
     if constexpr (decltype(k_c)::value == kCached) {
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk++) kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
+      for (int kk = 0; kk < KSTEPS; kk++)
+        kop[kk] = PERCH ? *reinterpret_cast<const i32x4*>(&sm.kc(slot)[krow][HALF * h + 16 * kk])
+                        : *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
     } else {
 #pragma unroll
       for (int t = 0; t < D / 16; t++) kop[t] = *reinterpret_cast<const i32x4*>(&ks.kr[krow][HALF * h + 8 * t]);
@@ -1097,6 +1164,9 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   const int c_beg = min(t_beg, n_ct), c_end = min(t_end, n_ct);
   const int r_beg = max(t_beg, n_ct) - n_ct, r_end = max(t_end, n_ct) - n_ct;
   if (c_end > c_beg) {
+    if constexpr (PERCH) {
+      if (computes) fill_qf();
+    }
     run(c_beg, c_end - c_beg, Kind<kCached>());
     if constexpr (!MASS_ONLY) {
       if (p.v_had && computes) unrotate();
@@ -1637,60 +1707,6 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   return KVQ_OK;
 }
 
-struct SignWords {
-  uint32_t w[4];
-};
-
-// q' = H q / sqrt(D) in fp32 for every query (keys quantized per channel re-quantize the
-// rotated query at every key group; rotating once per call spares each group the
-// transform). Two lanes per query, half a row each, in the order the attention kernel's
-// own rotation uses: butterflies inside the lane, then across the pair.
-template <int D>
-__global__ __launch_bounds__(256) void jb_rotate_q_kernel(const uint16_t* __restrict__ q, size_t rows,
-                                                          float* __restrict__ qrot, const SignWords sg) {
-  constexpr int HALF = D / 2;
-  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t row = t >> 1;
-  const int h = (int)(t & 1);
-  const bool ok = row < rows;
-  const uint4* src = reinterpret_cast<const uint4*>(q + (ok ? row : 0) * D + HALF * h);
-  uint32_t sgw[HALF / 32];
-#pragma unroll
-  for (int k = 0; k < HALF / 32; k++) sgw[k] = h ? sg.w[HALF / 32 + k] : sg.w[k];
-  float qv[HALF];
-#pragma unroll
-  for (int u = 0; u < HALF / 8; u++) {
-    const uint4 w = src[u];
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      const int j = 8 * u + 2 * e;
-      const uint32_t we = ww[e] ^ pair_sign_xor(sgw[j >> 5], j & 31);
-      qv[j] = __uint_as_float(we << 16);
-      qv[j + 1] = __uint_as_float(we & 0xFFFF0000u);
-    }
-  }
-#pragma unroll
-  for (int hh = 1; hh < HALF; hh <<= 1)
-#pragma unroll
-    for (int i = 0; i < HALF; i++)
-      if ((i & hh) == 0) {
-        const float a = qv[i], b = qv[i + hh];
-        qv[i] = a + b;
-        qv[i + hh] = a - b;
-      }
-  const float c = rsqrtf((float)D);
-#pragma unroll
-  for (int i = 0; i < HALF; i++) {
-    const float pv = __shfl_xor(qv[i], 1);
-    qv[i] = (h ? (pv - qv[i]) : (qv[i] + pv)) * c;
-  }
-  if (!ok) return;
-  float4* dst = reinterpret_cast<float4*>(qrot + row * D + HALF * h);
-#pragma unroll
-  for (int u = 0; u < HALF / 4; u++) dst[u] = make_float4(qv[4 * u], qv[4 * u + 1], qv[4 * u + 2], qv[4 * u + 3]);
-}
-
 // Combines the partial records of the n_split shares of each query: with M the largest
 // reference max, weights w = 2^(m - M); O = sum w acc / sum w (l_S + l_R), and the
 // masses from the weighted sums. One thread per (query, 4 output channels); G threads
@@ -1735,7 +1751,6 @@ __global__ __launch_bounds__(256) void jb_combine_kernel(const float* __restrict
 struct AttnPlan {
   int n_qblk, n_split;
   size_t part_bytes;  // workspace the split needs (0 for n_split == 1)
-  size_t qrot_bytes;  // workspace of the rotated queries (per-channel rotated keys), else 0
   int dec_shares;     // few queries: shares of the cached tiles per head (0: no decode path)
   size_t dec_bytes;   // workspace of the decode path's partial records
 };
@@ -1768,9 +1783,6 @@ AttnPlan plan_attn(const jb_attn_args* a) {
   pl.n_qblk = (a->n_q + kBM - 1) / kBM;
   pl.n_split = 1;
   pl.part_bytes = 0;
-  pl.qrot_bytes = (a->k_fmt.granularity == KVQ_PER_CHANNEL && a->k_fmt.hadamard && a->n_chunks > 0)
-                      ? (size_t)a->B * a->H * a->n_q * (size_t)a->d * sizeof(float)
-                      : 0;
   pl.dec_shares = 0;
   pl.dec_bytes = 0;
   int dev = 0, cus = 0;
@@ -1830,17 +1842,9 @@ Params fill_params(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
     p.v_sg[i] = a->v_fmt.signs[i];
   }
   p.k_group = PERCH ? a->k_fmt.group : 0;
-  // workspace: [rotated queries][split partials], each 16-byte aligned
-  char* ws = static_cast<char*>(a->workspace);
-  p.qrot = pl.qrot_bytes ? reinterpret_cast<const float*>(ws) : nullptr;
+  // workspace: the split partials (16-byte aligned)
   p.n_split = pl.n_split;
-  p.part = pl.n_split > 1 ? reinterpret_cast<float*>(ws + pl.qrot_bytes) : nullptr;
-  if (pl.qrot_bytes) {
-    const size_t rows = (size_t)a->B * a->H * a->n_q;
-    jb_rotate_q_kernel<D><<<(unsigned)((2 * rows + 255) / 256), 256, 0, st>>>(a->q, rows, reinterpret_cast<float*>(ws),
-                                                                              SignWords{{a->k_fmt.signs[0], a->k_fmt.signs[1],
-                                                                                         a->k_fmt.signs[2], a->k_fmt.signs[3]}});
-  }
+  p.part = pl.n_split > 1 ? static_cast<float*>(a->workspace) : nullptr;
   p.o = MASS_ONLY ? nullptr : a->o;
   p.mass_s = a->mass_s;
   p.mass_r = a->mass_r;
@@ -1867,7 +1871,6 @@ template <int D, int BITS, bool MASS_ONLY>
 int launch_decode(const jb_attn_args* a, const AttnPlan& pl0, hipStream_t st) {
   AttnPlan pl = pl0;
   pl.n_split = 1;
-  pl.qrot_bytes = 0;
   pl.part_bytes = 0;
   Params p = fill_params<D, MASS_ONLY, false>(a, pl, st);
   const int S = pl.dec_shares;
@@ -1904,14 +1907,12 @@ int dispatch(const jb_attn_args* a, void* stream) {
       return a->k_fmt.bits == 2 ? launch_decode<128, 2, MASS_ONLY>(a, pl, s) : launch_decode<128, 4, MASS_ONLY>(a, pl, s);
     return a->k_fmt.bits == 2 ? launch_decode<64, 2, MASS_ONLY>(a, pl, s) : launch_decode<64, 4, MASS_ONLY>(a, pl, s);
   }
-  // the workspace serves the rotated queries first, then the split partials; what does
-  // not fit is done without (in-kernel rotation, an unsplit grid)
-  if (pl.qrot_bytes && have < pl.qrot_bytes) pl.qrot_bytes = 0;
-  if (pl.n_split > 1 && have < pl.qrot_bytes + pl.part_bytes) {
+  // the workspace holds the split partials; without room the grid runs unsplit
+  if (pl.n_split > 1 && have < pl.part_bytes) {
     pl.n_split = 1;
     pl.part_bytes = 0;
   }
-  if ((pl.qrot_bytes || pl.n_split > 1) && !aligned16(a->workspace)) return KVQ_ERR_ALIGN;
+  if (pl.n_split > 1 && !aligned16(a->workspace)) return KVQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool perch = a->k_fmt.granularity == KVQ_PER_CHANNEL;
   if (a->correction == JB_CORR_EXACT && a->n_chunks > 0) {
@@ -1940,7 +1941,7 @@ template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
 int launch_batch(const jb_attn_args* calls, int n, hipStream_t st) {
   // One split count S for the whole batch, chosen as for a single call but over the
   // workgroups of all calls: rounds of the device times the longest share. It is used
-  // only when every call's workspace holds its rotated queries and its S partials.
+  // only when every call's workspace holds its S partials.
   AttnPlan pl[kMaxBatch];
   long long grid1 = 0, tiles = 0;
   for (int c = 0; c < n; c++) {
@@ -1959,7 +1960,7 @@ int launch_batch(const jb_attn_args* calls, int n, hipStream_t st) {
   for (int c = 0; c < n && S > 1; c++) {
     const jb_attn_args* a = &calls[c];
     const size_t part = (size_t)S * a->B * a->H * a->n_q * (size_t)(a->d + 4) * sizeof(float);
-    if (!a->workspace || !aligned16(a->workspace) || a->workspace_bytes < pl[c].qrot_bytes + part) S = 1;
+    if (!a->workspace || !aligned16(a->workspace) || a->workspace_bytes < part) S = 1;
   }
   BatchParams bp;
   bp.n = n;
@@ -1968,8 +1969,6 @@ int launch_batch(const jb_attn_args* calls, int n, hipStream_t st) {
     const jb_attn_args* a = &calls[c];
     pl[c].n_split = S;
     pl[c].part_bytes = S > 1 ? (size_t)S * a->B * a->H * a->n_q * (size_t)(a->d + 4) * sizeof(float) : 0;
-    const size_t have = a->workspace && aligned16(a->workspace) ? a->workspace_bytes : 0;
-    if (pl[c].qrot_bytes && have < pl[c].qrot_bytes) pl[c].qrot_bytes = 0;
     bp.p[c] = fill_params<D, MASS_ONLY, PERCH>(a, pl[c], st);
     bp.grid[c] = (int)(pl[c].n_qblk * a->B * a->H * S);
     bp.start[c] = (int)next;
@@ -2043,5 +2042,5 @@ extern "C" int jb_attn_mass(const jb_attn_args* a, void* stream) { return kvq::d
 extern "C" size_t jb_attn_workspace_bytes(const jb_attn_args* a) {
   if (kvq::validate_attn(a, false) != KVQ_OK && kvq::validate_attn(a, true) != KVQ_OK) return 0;
   const kvq::AttnPlan pl = kvq::plan_attn(a);
-  return pl.dec_shares ? pl.dec_bytes : pl.qrot_bytes + pl.part_bytes;
+  return pl.dec_shares ? pl.dec_bytes : pl.part_bytes;
 }

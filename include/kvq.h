@@ -184,13 +184,12 @@ int jb_attn_mass(const jb_attn_args* a, void* stream);
  * calls share the device, so calls that would each leave compute units idle fill it
  * together. The split over window shares (see jb_attn_workspace_bytes) is planned for
  * the batch as a whole, with one share count for every call, and taken only when each
- * call's workspace holds its rotated queries and its partials for that count; otherwise
+ * call's workspace holds its partials for that count; otherwise
  * no call is split, and each computes exactly what jb_attn_fwd (jb_attn_mass) would for
  * it unsplit. Calls must agree on d, bits, key
  * granularity (and group), and on whether correction is JB_CORR_EXACT; shapes, windows,
- * rotation flags and signs, softmax scale and the other correction modes may differ. A
- * call's workspace, if it holds at least its rotated queries (per-channel keys), is used
- * for them. calls points to n_calls host structs, 1 <= n_calls <= KVQ_BATCH_MAX.
+ * rotation flags and signs, softmax scale and the other correction modes may differ.
+ * calls points to n_calls host structs, 1 <= n_calls <= KVQ_BATCH_MAX.
  * Errors: the first failing call's jb_attn_fwd (jb_attn_mass) status, KVQ_ERR_NULL
  * (calls NULL), KVQ_ERR_SHAPE (n_calls out of range, too many workgroups in total),
  * KVQ_ERR_UNSUPPORTED (calls that disagree as above). */

@@ -185,8 +185,8 @@ def test_per_channel_keys_all_rows(shape, bits, correction):
 
 @pytest.mark.parametrize("shape", PERCH[:2], ids=lambda s: "x".join(str(v) for v in s.values()))
 def test_per_channel_keys_without_workspace(shape):
-    """Per-channel keys with no workspace: the kernel rotates the query itself at every key
-    group (with one, a pre-pass rotates every query once and the call may also split)."""
+    """Per-channel keys with and without a workspace (with one the call may split; a
+    workspace too small for the split partials runs unsplit)."""
     w = synth.Workload("perch", **shape, bits=2, k_dist="t3", k_granularity="channel", seed=11)
     print(f"attn per-channel {shape} without workspace", flush=True)
     x = synth.draw_all(w)
@@ -194,12 +194,11 @@ def test_per_channel_keys_without_workspace(shape):
     assert run_gpu.last_workspace_bytes == 0
     b = run_gpu(x, w, split=True)
     assert run_gpu.last_workspace_bytes > 0
-    # room for the rotated queries only: rotation pre-pass, no split
-    qrot_bytes = w.B * w.H * w.n_q * w.d * 4
-    assert run_gpu.wanted_workspace_bytes > qrot_bytes, "expected a split plan as well"
-    c = run_gpu(x, w, ws_bytes=qrot_bytes)
+    # a workspace one record short of the split: the call runs unsplit
+    assert run_gpu.wanted_workspace_bytes > 16, "expected a split plan"
+    c = run_gpu(x, w, ws_bytes=run_gpu.wanted_workspace_bytes - 16)
     Or, PSr, PRr = run_oracle(x, w)
-    for label, r in (("no workspace", a), ("workspace", b), ("rotation only", c)):
+    for label, r in (("no workspace", a), ("workspace", b), ("short workspace", c)):
         assert_attention_close(r[0], Or, f"perch {label}")
         assert_mass_close(r[1], r[2], PSr, PRr, f"perch {label}")
 

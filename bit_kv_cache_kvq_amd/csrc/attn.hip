@@ -216,7 +216,6 @@ struct Smem : SmemSlots<D> {
   alignas(16) typename T::PSlot prm[3];
   alignas(16) typename T::ZSlot z[3];
   alignas(16) float a_stream[kNS];
-  __device__ typename T::KCodes& kc(int s) { return k[s].c; }
 };
 
 // Per-channel keys also keep each stream's rotated queries in LDS during the cached tiles,
@@ -678,7 +677,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           const uint32_t w0 = kpre[i].x, w1 = kpre[i].y;
           lo = make_uint4(w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu);
         }
-        if constexpr (PERCH)
+        if constexpr (PERCH)  // packed code slots
           *reinterpret_cast<uint4*>(&sm.kc(slot)[tok][16 * ui]) = lo;
         else
           *reinterpret_cast<uint4*>(&ks.c[tok][16 * ui]) = lo;
@@ -872,9 +871,12 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     kbop = sm.prm[slot].kb[32 * mb + col][h];
     if constexpr (decltype(k_c)::value == kCached) {
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk++)
-        kop[kk] = PERCH ? *reinterpret_cast<const i32x4*>(&sm.kc(slot)[krow][HALF * h + 16 * kk])
-                        : *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
+      for (int kk = 0; kk < KSTEPS; kk++) {
+        if constexpr (PERCH)
+          kop[kk] = *reinterpret_cast<const i32x4*>(&sm.kc(slot)[krow][HALF * h + 16 * kk]);
+        else
+          kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
+      }
     } else {
 #pragma unroll
       for (int t = 0; t < D / 16; t++) kop[t] = *reinterpret_cast<const i32x4*>(&ks.kr[krow][HALF * h + 8 * t]);
@@ -1748,6 +1750,74 @@ __global__ __launch_bounds__(256) void jb_combine_kernel(const float* __restrict
   }
 }
 
+// The same merge for many records per query (the few-query path: one record per share of
+// the window, tens of shares): one workgroup per query, its threads split over channel
+// groups (G of 4 channels) and record slices (R = 256 / G, records r, r + R, ...). Each
+// thread merges its slice against the slice's own largest reference max; the slices are
+// then combined through LDS against the largest of all.
+template <int D, bool MASS_ONLY>
+__global__ __launch_bounds__(256) void jb_merge_records_kernel(const float* __restrict__ part, int n_rec, size_t rows,
+                                                               float* __restrict__ o, float* __restrict__ mass_s,
+                                                               float* __restrict__ mass_r) {
+  constexpr int G = D / 4, R = 256 / G;
+  __shared__ float4 sa[R][G];
+  __shared__ float sm_m[R], sm_s[R], sm_r[R];
+  const size_t row = blockIdx.x;
+  const int cg = threadIdx.x % G, r = threadIdx.x / G;
+  const size_t stride = rows * (D + 4);
+  const float* rec0 = part + row * (D + 4);
+  float M = -INFINITY;
+  for (int sp = r; sp < n_rec; sp += R) M = fmaxf(M, rec0[sp * stride + D]);
+  float ls = 0.f, lr = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = r; sp < n_rec; sp += R) {
+    const float* rec = rec0 + sp * stride;
+    const float4 st = *reinterpret_cast<const float4*>(rec + D);
+    const float w = exp2f(st.x - M);
+    ls = fmaf(w, st.y, ls);
+    lr = fmaf(w, st.z, lr);
+    if constexpr (!MASS_ONLY) {
+      const float4 v = *reinterpret_cast<const float4*>(rec + 4 * cg);
+      a.x = fmaf(w, v.x, a.x);
+      a.y = fmaf(w, v.y, a.y);
+      a.z = fmaf(w, v.z, a.z);
+      a.w = fmaf(w, v.w, a.w);
+    }
+  }
+  sa[r][cg] = a;
+  if (cg == 0) {
+    sm_m[r] = M;
+    sm_s[r] = ls;
+    sm_r[r] = lr;
+  }
+  __syncthreads();
+  if (r != 0) return;
+  float Mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < R; i++) Mx = fmaxf(Mx, sm_m[i]);
+  float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+  float ts = 0.f, tr = 0.f;
+#pragma unroll
+  for (int i = 0; i < R; i++) {
+    if (sm_m[i] == -INFINITY) continue;  // a slice without records
+    const float f = exp2f(sm_m[i] - Mx);
+    ts = fmaf(f, sm_s[i], ts);
+    tr = fmaf(f, sm_r[i], tr);
+    const float4 v = sa[i][cg];
+    t.x = fmaf(f, v.x, t.x);
+    t.y = fmaf(f, v.y, t.y);
+    t.z = fmaf(f, v.z, t.z);
+    t.w = fmaf(f, v.w, t.w);
+  }
+  const float inv = 1.f / (ts + tr);
+  if constexpr (!MASS_ONLY)
+    *reinterpret_cast<float4*>(o + row * D + 4 * cg) = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  if (cg == 0 && mass_s) {
+    mass_s[row] = ts * inv;
+    mass_r[row] = tr * inv;
+  }
+}
+
 struct AttnPlan {
   int n_qblk, n_split;
   size_t part_bytes;  // workspace the split needs (0 for n_split == 1)
@@ -1888,9 +1958,7 @@ int launch_decode(const jb_attn_args* a, const AttnPlan& pl0, hipStream_t st) {
     jb_attn_kernel<D, BITS, MASS_ONLY, false, false><<<(unsigned)(pl.n_qblk * a->B * a->H), kThreads, 0, st>>>(pc);
     n_rec++;
   }
-  constexpr int G = MASS_ONLY ? 1 : D / 4;
-  jb_combine_kernel<D, G, MASS_ONLY><<<(unsigned)((rows * G + 255) / 256), 256, 0, st>>>(part, n_rec, rows, p.o,
-                                                                                         p.mass_s, p.mass_r);
+  jb_merge_records_kernel<D, MASS_ONLY><<<(unsigned)rows, 256, 0, st>>>(part, n_rec, rows, p.o, p.mass_s, p.mass_r);
   return launch_status();
 }
 

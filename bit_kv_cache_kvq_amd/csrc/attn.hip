@@ -563,6 +563,9 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));  // stream-wide max
     const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
     a_ch = mxa > 0.f ? scale_l2 * (mxa * sq0 / kQFix) : 0.f;
+    // zero-point sum sum_c q~_c z_gc from the unrounded q~ (one mixed fma per channel; the
+    // rounding of q_f it leaves out shifts all of the group's logits alike, by ~1e-5 of
+    // s max|q~|)
     float zs = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; kk++) {
@@ -586,7 +589,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           const int c = kperm<BITS>(j, b);
           const float f = fmaf(qv[16 * kk + c], inv, kRoundMagic);
           fb[b] = __float_as_uint(f);
-          zs = fmaf(f - kRoundMagic, (float)zt[c], zs);  // q_f, exact
+          zs = fmaf(qv[16 * kk + c], (float)zt[c], zs);
         }
         const uint32_t p0 = __builtin_amdgcn_perm(fb[1], fb[0], 0x05040100u);  // int16 pairs
         const uint32_t p1 = __builtin_amdgcn_perm(fb[3], fb[2], 0x05040100u);
@@ -599,7 +602,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     }
     zs += xor32(zs);
     const float G = EXACT ? bx * kLog2e : p.correction ? p.s * p.s * (sq0 * sq0) * ss * (1.f / 24.f) * kLog2e : 0.f;
-    c_grp = -a_ch * zs - G;
+    c_grp = -a_ch * inv * zs - G;
     write_mslot();
   };
 

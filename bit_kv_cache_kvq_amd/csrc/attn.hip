@@ -1283,6 +1283,152 @@ __device__ inline void load_words(const __amdgpu_buffer_rsrc_t rs, uint32_t off,
   }
 }
 
+// The current chunk of a few-query call as one more share of the decode grid (one wave):
+// bf16 QK^T (exact products, no correction), the bias MFMA for -m and the padding mask, fp16
+// P and values, written as a partial record (l_R, natural basis) for the merge. Key rows
+// are read straight into MFMA operands: lane (h, col) holds channels HALF h .. of the
+// block's key in M row col, as the main kernel's current tiles do from LDS.
+template <int D, bool MASS_ONLY>
+__device__ KVQ_INLINE void decode_current(const Params& p, const int bh, const int rec) {
+  constexpr int HALF = D / 2;
+  constexpr int CBLK = D / 32;
+  const int lane = threadIdx.x;
+  const int h = lane >> 5, col = lane & 31;
+  const bool q_ok = col < p.n_q;
+  const int qi = q_ok ? col : 0;
+  const float scale_l2 = p.s * kLog2e;
+  const uint16_t* kr = p.k_cur + (size_t)bh * p.n_r * D;
+  const uint16_t* vr = p.v_cur + (size_t)bh * p.n_r * D;
+  bf16x8 qop[D / 16];
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(p.q + ((size_t)bh * p.n_q + qi) * D + HALF * h);
+#pragma unroll
+    for (int t = 0; t < D / 16; t++) qop[t] = __builtin_bit_cast(bf16x8, q_ok ? qrow[t] : make_uint4(0, 0, 0, 0));
+  }
+  f16x8 qbias;
+#pragma unroll
+  for (int e = 0; e < 8; e++) qbias[e] = (_Float16)0.f;
+  if (h) qbias[2] = (_Float16)(-kMaskLogit);
+  float m_run = -INFINITY;
+  auto set_m = [&](float mx) KVQ_INLINE {
+    _Float16 mh, ml;
+    split16(-mx, mh, ml);
+    m_run = -((float)mh + (float)ml);
+    qbias[0] = h ? mh : qbias[0];
+    qbias[1] = h ? ml : qbias[1];
+  };
+  float l_r = 0.f;
+  f32x16 acc[CBLK];
+#pragma unroll
+  for (int c = 0; c < CBLK; c++) acc[c] = f32x16{};
+  uint32_t pb[2][4];
+  const int n_rt = (p.n_r + kBN - 1) / kBN;
+  for (int U = 0; U < n_rt; U++) {
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++) {
+      const int t0 = U * kBN + 32 * mb;
+      const int tok = t0 + mrow_key(col);
+      const bool kv = tok < p.n_r;
+      const uint4* krow = reinterpret_cast<const uint4*>(kr + (size_t)min(tok, p.n_r - 1) * D + HALF * h);
+      bf16x8 kop[D / 16];
+#pragma unroll
+      for (int t = 0; t < D / 16; t++) kop[t] = __builtin_bit_cast(bf16x8, kv ? krow[t] : make_uint4(0, 0, 0, 0));
+      const uint32_t one = 0x3C00u;
+      const uint4 kbop = h ? make_uint4(one | (one << 16), kv ? 0u : one, 0u, 0u) : make_uint4(0, 0, 0, 0);
+      const f32x16 zf = {};
+      const f32x16 cbv = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kbop), qbias, zf, 0, 0, 0);
+      f32x16 sc = {};
+#pragma unroll
+      for (int t = 0; t < D / 16; t++) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[t], qop[t], sc, 0, 0, 0);
+      float x[16];
+#pragma unroll
+      for (int v = 0; v < 16; v++) x[v] = fmaf(scale_l2, sc[v], cbv[v]);
+      auto pairs = [&](float off) KVQ_INLINE {
+        float ls2[2] = {0.f, 0.f};
+        const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+        for (int v2 = 0; v2 < 8; v2++) {
+          const uint32_t pr = pack_f16x2(exp2_(x[2 * v2] - off), exp2_(x[2 * v2 + 1] - off));
+          pb[v2 >> 2][v2 & 3] = pr;
+          ls2[v2 & 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pr), ones, ls2[v2 & 1], false);
+        }
+        return ls2[0] + ls2[1];
+      };
+      float lsum;
+      if (__builtin_amdgcn_readfirstlane(m_run == -INFINITY ? 1 : 0)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; v++) mx = fmaxf(mx, x[v]);
+        mx = fmaxf(mx, xor32(mx));
+        set_m(mx + kHeadroom);
+        lsum = pairs(m_run);
+      } else {
+        lsum = pairs(0.f);
+        const bool raise = !(lsum <= kPmax);
+        if (__ballot(raise) != 0) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int v = 0; v < 16; v++) mx = fmaxf(mx, x[v]);
+          mx = fmaxf(mx, xor32(mx));
+          const float partner_raise = xor32(raise ? 1.f : 0.f);
+          const bool up = raise || partner_raise != 0.f;
+          const float m_old = m_run;
+          set_m(up ? m_old + mx : m_old);
+          const float scl = exp2_(m_old - m_run);
+          l_r *= scl;
+          if constexpr (!MASS_ONLY) {
+#pragma unroll
+            for (int c = 0; c < CBLK; c++)
+#pragma unroll
+              for (int v = 0; v < 16; v++) acc[c][v] *= scl;
+          }
+          lsum = pairs(m_run - m_old);
+        }
+      }
+      l_r += lsum;
+      if constexpr (!MASS_ONLY) {
+        // value operands: element i of lane (h, col) is token 4 h + (i >> 1) + 8 (i & 1) of
+        // 16-key group ks, channel 32 c + col (the P operand's key order)
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+          f16x8 vop[CBLK];
+#pragma unroll
+          for (int c = 0; c < CBLK; c++) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i2 = 0; i2 < 4; i2++) {
+              float f[2];
+#pragma unroll
+              for (int e = 0; e < 2; e++) {
+                const int tv = t0 + 16 * ks + 4 * h + i2 + 8 * e;
+                const uint16_t b = vr[(size_t)min(tv, p.n_r - 1) * D + 32 * c + col];
+                f[e] = tv < p.n_r ? __uint_as_float((uint32_t)b << 16) : 0.f;
+              }
+              w[i2] = pack_f16x2(f[0], f[1]);
+            }
+            vop[c] = __builtin_bit_cast(f16x8, make_uint4(w[0], w[1], w[2], w[3]));
+          }
+          const f16x8 bop = __builtin_bit_cast(f16x8, make_uint4(pb[ks][0], pb[ks][1], pb[ks][2], pb[ks][3]));
+#pragma unroll
+          for (int c = 0; c < CBLK; c++) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vop[c], bop, acc[c], 0, 0, 0);
+        }
+      }
+    }
+  }
+  const float lr = l_r + xor32(l_r);
+  if (!q_ok) return;
+  float* out = p.part + (((size_t)rec * p.B * p.H + bh) * p.n_q + qi) * (D + 4);
+  if constexpr (!MASS_ONLY) {
+#pragma unroll
+    for (int c = 0; c < CBLK; c++)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; v4++)
+        *reinterpret_cast<float4*>(out + 32 * c + 8 * v4 + 4 * h) =
+            make_float4(acc[c][4 * v4], acc[c][4 * v4 + 1], acc[c][4 * v4 + 2], acc[c][4 * v4 + 3]);
+  }
+  if (h == 0) *reinterpret_cast<float4*>(out + D) = make_float4(m_run, 0.f, lr, 0.f);
+}
+
 template <int D, int BITS, bool MASS_ONLY>
 __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const int shares) {
   constexpr int HALF = D / 2;
@@ -1296,7 +1442,12 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
   __shared__ SmemDec sm;
   const int lane = threadIdx.x;
   const int h = lane >> 5, col = lane & 31;
-  const int bh = blockIdx.x / shares, sp = blockIdx.x % shares;
+  const int per = shares + (p.n_r > 0 ? 1 : 0);  // the last share of a head: its current chunk
+  const int bh = blockIdx.x / per, sp = blockIdx.x % per;
+  if (sp == shares) {
+    decode_current<D, MASS_ONLY>(p, bh, shares);
+    return;
+  }
   const bool q_ok = col < p.n_q;
   const int qi = q_ok ? col : 0;
   const float scale_l2 = p.s * kLog2e;
@@ -1865,12 +2016,13 @@ AttnPlan plan_attn(const jb_attn_args* a) {
     return pl;
   }
   // At most 32 queries (one stream) with per-token keys and a cached window: the decode
-  // path, with as many one-wave shares as fit on the device at once (two per SIMD)
+  // path, with as many one-wave shares (the window's, plus one per head for its current
+  // chunk) as fit on the device at once (two per SIMD)
   const long long n_ct = (long long)a->n_chunks * (chunk_pad(a->chunk_len) / kBN);
   if (a->n_q <= 32 && a->k_fmt.granularity == KVQ_PER_TOKEN && a->correction != JB_CORR_EXACT && n_ct > 0) {
     const long long bhc = (long long)a->B * a->H;
-    const long long S = std::min(n_ct, std::max(1LL, 8LL * cus / bhc));
-    if (S * bhc <= 0x7FFFFFFFLL) {
+    const long long S = std::min(n_ct, std::max(1LL, 8LL * cus / bhc - (a->n_r > 0 ? 1 : 0)));
+    if ((S + 1) * bhc <= 0x7FFFFFFFLL) {
       pl.dec_shares = (int)S;
       pl.dec_bytes = (size_t)(S + (a->n_r > 0 ? 1 : 0)) * bhc * a->n_q * (size_t)(a->d + 4) * sizeof(float);
     }
@@ -1938,8 +2090,8 @@ int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   return launch_status();
 }
 
-// Few queries: the decode kernel over the cached window (one partial record per share),
-// the main kernel over the current chunk as one more partial record, then the merge.
+// Few queries: the decode kernel over the cached window (one partial record per share)
+// and, in the same grid, over the current chunk (one more record per query), then the merge.
 template <int D, int BITS, bool MASS_ONLY>
 int launch_decode(const jb_attn_args* a, const AttnPlan& pl0, hipStream_t st) {
   AttnPlan pl = pl0;
@@ -1950,17 +2102,8 @@ int launch_decode(const jb_attn_args* a, const AttnPlan& pl0, hipStream_t st) {
   const size_t rows = (size_t)a->B * a->H * a->n_q;
   float* part = static_cast<float*>(a->workspace);
   p.part = part;
-  jb_decode_kernel<D, BITS, MASS_ONLY><<<(unsigned)(S * a->B * a->H), 64, 0, st>>>(p, S);
-  int n_rec = S;
-  if (a->n_r > 0) {
-    Params pc = p;
-    pc.n_chunks = 0;
-    pc.n_wchunks = 0;
-    pc.part = part + (size_t)S * rows * (D + 4);
-    pc.n_split = 1;
-    jb_attn_kernel<D, BITS, MASS_ONLY, false, false><<<(unsigned)(pl.n_qblk * a->B * a->H), kThreads, 0, st>>>(pc);
-    n_rec++;
-  }
+  const int n_rec = S + (a->n_r > 0 ? 1 : 0);  // the window's shares, then the current chunk
+  jb_decode_kernel<D, BITS, MASS_ONLY><<<(unsigned)(n_rec * a->B * a->H), 64, 0, st>>>(p, S);
   jb_merge_records_kernel<D, MASS_ONLY><<<(unsigned)rows, 256, 0, st>>>(part, n_rec, rows, p.o, p.mass_s, p.mass_r);
   return launch_status();
 }

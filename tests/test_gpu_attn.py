@@ -633,7 +633,7 @@ def test_decode_path_all_rows(shape, bits):
 def test_decode_path_variants():
     w = synth.Workload("dec", B=1, H=2, d=128, n_q=20, chunk_len=200, n_chunks=5, seed=61)
     x = synth.draw_all(w)
-    print("attn decode: no current chunk, masses only, signs, no correction", flush=True)
+    print("attn decode: no current chunk, masses only, signs, no correction, long current chunk", flush=True)
     # no current chunk: the cached shares only
     xn = dict(x, k_cur=x["k_cur"][:, :, :0], v_cur=x["v_cur"][:, :, :0])
     wn = w.replace(n_q=20)
@@ -651,6 +651,15 @@ def test_decode_path_variants():
     Or, PSr, PRr = run_oracle(x, w, correction="none", k_signs=ks, v_signs=vs)
     assert_attention_close(O, Or, "decode signs")
     assert_mass_close(PS, PR, PSr, PRr, "decode signs")
+    # a current chunk longer than the query count: several current tiles, the last ragged
+    wl = synth.Workload("dec", B=1, H=2, d=128, n_q=150, chunk_len=200, n_chunks=5, seed=62)
+    xl = synth.draw_all(wl)
+    xs = dict(xl, q=xl["q"][:, :, :20])
+    O, PS, PR = run_gpu(xs, wl)
+    assert run_gpu.last_workspace_bytes > 0, "expected the decode path"
+    Or, PSr, PRr = run_oracle(xs, wl)
+    assert_attention_close(O, Or, "decode long current chunk")
+    assert_mass_close(PS, PR, PSr, PRr, "decode long current chunk")
     # the exact correction takes the main kernel (no decode workspace is asked for)
     O, PS, PR = run_gpu(x, w, correction=2)
     Or, PSr, PRr = run_oracle(x, w, correction="exact")

@@ -114,7 +114,7 @@ def main():
                     help="only run a device copy of this many MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by head with no communication; see the design notes)", file=sys.stderr)
         sys.exit(2)
 

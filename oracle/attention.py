@@ -8,7 +8,7 @@ b is subtracted from the scores of cached keys before the softmax; the
 cached-block and current-chunk attention masses P_S and P_R (Fig. 2 caption)
 are the shares of the softmax mass that fall on each block.
 
-Readings (listed in the design doc): no causal mask inside the current chunk (every
+Readings (listed in the design notes): no causal mask inside the current chunk (every
 query sees the whole window and the whole current chunk); softmax scale
 s = 1/sqrt(d); the correction is applied in the same scaled-score units the
 softmax sees (``correction.py``).

@@ -7,7 +7,7 @@ Fig. 3 caption in §1 (zero-mean uniform quantization noise delta on a score;
 E[e^(s+delta)] exceeds e^s by convexity of exp; subtracting b moves E[e^(s_hat-b)]
 back toward e^s). The derivation section itself (§4) is not among the pages, so
 the correction is derived here from that model; this is the plainest reading
-and it is listed in DESIGN.md.
+and it is listed in the design notes.
 
 Derivation. A cached key k is stored as k_hat = k + eps in the rotated basis
 (Eq. (1)), with eps_c independent and uniform on [-Delta_c/2, Delta_c/2]

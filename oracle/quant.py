@@ -8,9 +8,10 @@ Delta and z are chosen to cover the group's whole [min, max] range. §3
 group of channels of a token, or per tensor; keys may also share one pair per
 channel over a group of tokens (the KIVI-style per-channel key scheme named in
 §2). The paper quantizes keys and values after a Hadamard rotation (Fig. 1
-caption: "asymmetric INT2 (QuaRot+RTN)" on keys and values).
+caption: asymmetric INT2 with the QuaRot rotation and round-to-nearest, on keys and
+values).
 
-Readings where the pages leave a step open (each is also listed in the design doc):
+Readings where the pages leave a step open (each is also listed in the design notes):
 
 * Delta = (max - min) / (2^B - 1), stored as fp16 (round to nearest even);
   z = round(-min / Delta), an integer, not clamped to [0, 2^B - 1], stored as

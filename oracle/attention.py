@@ -28,7 +28,7 @@ import numpy as np
 from . import correction as corr
 from .hadamard import rotate_f64
 from .quant import (Format, bf16_to_f32, dequant_window, pack_window, step_per_channel_key,
-                    step_per_token_key)
+                    step_per_token_key, step_token_group_key)
 
 
 def attend_head(q, k_c, v_c, k_r, v_r, s, bias=None, block=256):
@@ -125,7 +125,11 @@ def _bias_fn(q, cache, b, h, chunk_len, k_fmt: Format, s, correction):
         if correction == "taylor":
             return lambda rows: corr.bias_taylor_per_token(q_rot[rows], delta, s)
         return lambda rows: corr.bias_exact(q_rot[rows], delta, s)
-    delta = step_per_channel_key(cache["k_scale"][b:b + 1, h:h + 1], chunk_len, n_chunks, k_fmt.group)[0, 0]
+    if k_fmt.granularity == "token_group":
+        # a step per (key, channel): the general form b = s^2 sum_c q'_c^2 Delta_jc^2 / 24
+        delta = step_token_group_key(cache["k_scale"][b:b + 1, h:h + 1], chunk_len, n_chunks, k_fmt.group)[0, 0]
+    else:
+        delta = step_per_channel_key(cache["k_scale"][b:b + 1, h:h + 1], chunk_len, n_chunks, k_fmt.group)[0, 0]
     if correction == "taylor":
         return lambda rows: corr.bias_taylor_per_channel(q_rot[rows], delta, s)
     return lambda rows: corr.bias_exact(q_rot[rows], delta, s)

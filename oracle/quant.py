@@ -43,6 +43,9 @@ Storage layouts (the library's documented format, restated here independently):
   holds tokens c*u .. c*u + c - 1, token c*u + i in bits [B*i, B*i + B).
   Window array shape [B, H, n_chunks * chunk_pad / 64, d, 64 / c].
 * Per-token scale and zero: fp16 [B, H, n_chunks * chunk_pad].
+  Group-wise per token (§3's third granularity: each token's d channels split into
+  groups of g = ``group`` channels, group j holding its own (Delta_ij, z_ij)):
+  fp16 [B, H, n_chunks * chunk_pad, d / g], pad tokens 0.
   Per-channel (keys only): fp16 [B, H, n_chunks * ceil(chunk_len / group), d];
   groups restart at each chunk's first token.
 """
@@ -60,8 +63,8 @@ TOKEN_BLOCK = 64
 @dataclasses.dataclass(frozen=True)
 class Format:
     bits: int = 2                 # 2 or 4
-    granularity: str = "token"    # "token" | "channel" (channel: keys only)
-    group: int = 128              # tokens per channel group
+    granularity: str = "token"    # "token" | "token_group" | "channel" (channel: keys only)
+    group: int = 128              # channel: tokens per channel group; token_group: channels per group
     hadamard: bool = True
     role: str = "key"             # "key" (token-major words) | "value" (channel-major blocks)
     signs: tuple = ()             # randomized rotation H diag(s): d values of +1/-1; () is s = 1
@@ -102,8 +105,10 @@ def quantize_lastaxis(y: np.ndarray, bits: int):
 def quantize_chunk(x_bits: np.ndarray, fmt: Format):
     """Quantize one chunk x [B, H, n, d] (bf16 bits) -> codes [B,H,n,d], scale, zero.
 
-    Per-token: scale, zero are [B, H, n]. Per-channel: [B, H, ceil(n/group), d],
-    group g covering tokens [g*group, min(n, (g+1)*group)).
+    Per-token: scale, zero are [B, H, n]. Group-wise per token: [B, H, n, d/group],
+    group j of a token covering channels [j*group, (j+1)*group) of the stored basis.
+    Per-channel: [B, H, ceil(n/group), d], group g covering tokens
+    [g*group, min(n, (g+1)*group)).
     """
     x = bf16_to_f32(x_bits)
     if fmt.signs and not fmt.hadamard:
@@ -113,6 +118,11 @@ def quantize_chunk(x_bits: np.ndarray, fmt: Format):
     if fmt.granularity == "token":
         codes, delta, z = quantize_lastaxis(y, fmt.bits)
         return codes, delta, z
+    if fmt.granularity == "token_group":
+        if d % fmt.group:
+            raise ValueError("channel group does not divide d")
+        codes, delta, z = quantize_lastaxis(y.reshape(B, H, n, d // fmt.group, fmt.group), fmt.bits)
+        return codes.reshape(B, H, n, d), delta, z
     if fmt.granularity != "channel":
         raise ValueError(fmt.granularity)
     G = -(-n // fmt.group)
@@ -183,6 +193,9 @@ def pack_window(x_bits: np.ndarray, chunk_len: int, fmt: Format):
     if fmt.granularity == "token":
         scale = np.zeros((B, H, nch * cp), dtype=np.float16)
         zero = np.zeros((B, H, nch * cp), dtype=np.float16)
+    elif fmt.granularity == "token_group":
+        scale = np.zeros((B, H, nch * cp, d // fmt.group), dtype=np.float16)
+        zero = np.zeros((B, H, nch * cp, d // fmt.group), dtype=np.float16)
     else:
         G = -(-chunk_len // fmt.group)
         scale = np.zeros((B, H, nch * G, d), dtype=np.float16)
@@ -190,7 +203,7 @@ def pack_window(x_bits: np.ndarray, chunk_len: int, fmt: Format):
     for ci in range(nch):
         codes, delta, z = quantize_chunk(x_bits[:, :, ci * chunk_len:(ci + 1) * chunk_len, :], fmt)
         codes_pad[:, :, ci * cp: ci * cp + chunk_len, :] = codes
-        if fmt.granularity == "token":
+        if fmt.granularity in ("token", "token_group"):
             scale[:, :, ci * cp: ci * cp + chunk_len] = delta.astype(np.float16)
             zero[:, :, ci * cp: ci * cp + chunk_len] = z.astype(np.float16)
         else:
@@ -220,6 +233,10 @@ def dequant_window(words, scale, zero, chunk_len: int, n_chunks: int, fmt: Forma
         if fmt.granularity == "token":
             dl = scale[:, :, ci * cp: ci * cp + chunk_len].astype(np.float64)[..., None]
             zz = zero[:, :, ci * cp: ci * cp + chunk_len].astype(np.float64)[..., None]
+        elif fmt.granularity == "token_group":
+            # channel c of a token takes its group's pair (c // g)
+            dl = np.repeat(scale[:, :, ci * cp: ci * cp + chunk_len].astype(np.float64), fmt.group, axis=-1)
+            zz = np.repeat(zero[:, :, ci * cp: ci * cp + chunk_len].astype(np.float64), fmt.group, axis=-1)
         else:
             G = -(-chunk_len // fmt.group)
             tok_group = np.arange(chunk_len) // fmt.group
@@ -234,6 +251,15 @@ def step_per_token_key(scale, chunk_len: int, n_chunks: int) -> np.ndarray:
     cp = chunk_pad(chunk_len)
     s = scale.astype(np.float64).reshape(scale.shape[0], scale.shape[1], n_chunks, cp)[..., :chunk_len]
     return s.reshape(scale.shape[0], scale.shape[1], n_chunks * chunk_len)
+
+
+def step_token_group_key(scale, chunk_len: int, n_chunks: int, group: int) -> np.ndarray:
+    """Group-wise per-token key steps expanded to channels: Delta_{j,c} = Delta_{j, c // g}
+    (float64), [B, H, n_c, d]."""
+    cp = chunk_pad(chunk_len)
+    B, H, _, G = scale.shape
+    s = scale.astype(np.float64).reshape(B, H, n_chunks, cp, G)[:, :, :, :chunk_len, :]
+    return np.repeat(s.reshape(B, H, n_chunks * chunk_len, G), group, axis=-1)
 
 
 def step_per_channel_key(scale, chunk_len: int, n_chunks: int, group: int) -> np.ndarray:

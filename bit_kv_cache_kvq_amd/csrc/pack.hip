@@ -2,7 +2,8 @@
 //
 // Paper: "Quantized Keys Steal Attention" (arXiv 2605.26266), §3 -- Hadamard rotation,
 // asymmetric round-to-nearest integer quantization (Eq. (1)) and its granularities
-// (per token; per channel over a group of tokens for keys). The exact float32 operation
+// (per token; per group of channels of a token; per channel over a group of tokens for
+// keys). The exact float32 operation
 // order is the one stated in include/kvq.h at kvq_format; it makes codes, steps and zero
 // points reproducible bit for bit. This translation unit is built with -ffp-contract=off
 // and correctly rounded float32 division.
@@ -122,12 +123,15 @@ __device__ inline void store_key_words(uint32_t* __restrict__ dst_token, int lt,
   }
 }
 
-// Per-token quantization of one 64-token block of the padded chunk.
-template <int D, int BITS, int ROLE>
+// Per-token quantization of one 64-token block of the padded chunk; with CG < D, each
+// token's channels form groups of CG (group-wise per token), one (Delta, z) pair each.
+template <int D, int BITS, int ROLE, int CG = D>
 __global__ __launch_bounds__(64 * D / 16) void pack_token_kernel(
     const uint16_t* __restrict__ x, int n, int n_chunks, int chunk_idx, int hadamard, const SignBits sg,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale, uint16_t* __restrict__ zero) {
   constexpr int LPT = D / 16;            // lanes per token
+  constexpr int LPG = CG / 16;           // lanes per channel group
+  constexpr int NG = D / CG;             // (Delta, z) pairs per token
   constexpr int CPW = 32 / BITS;         // codes per word
   const int tid = threadIdx.x;
   const int tl = tid / LPT, lt = tid % LPT;
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(64 * D / 16) void pack_token_kernel(
     mx = fmaxf(mx, y[i]);
   }
 #pragma unroll
-  for (int hl = 1; hl < LPT; hl <<= 1) {
+  for (int hl = 1; hl < LPG; hl <<= 1) {
     mn = fminf(mn, __shfl_xor(mn, hl));
     mx = fmaxf(mx, __shfl_xor(mx, hl));
   }
@@ -159,9 +163,10 @@ __global__ __launch_bounds__(64 * D / 16) void pack_token_kernel(
   for (int i = 0; i < 16; i++) c[i] = valid ? code_of<BITS>(y[i], qp.delta, qp.z) : 0u;
 
   const size_t tok_w = (size_t)chunk_idx * cp + t;
-  if (lt == 0) {
-    scale[bh * n_tot + tok_w] = valid ? qp.scale_bits : (uint16_t)0;
-    zero[bh * n_tot + tok_w] = valid ? qp.zero_bits : (uint16_t)0;
+  if (lt % LPG == 0) {
+    const size_t at = (bh * n_tot + tok_w) * NG + lt / LPG;
+    scale[at] = valid ? qp.scale_bits : (uint16_t)0;
+    zero[at] = valid ? qp.zero_bits : (uint16_t)0;
   }
   if (ROLE == KVQ_ROLE_KEY) {
     store_key_words<D, BITS>(codes + (bh * n_tot + tok_w) * (D / CPW), lt, c);
@@ -244,6 +249,7 @@ int validate_format(const kvq_format* f) {
   if (!f->hadamard && (f->signs[0] | f->signs[1] | f->signs[2] | f->signs[3])) return KVQ_ERR_UNSUPPORTED;
   if (f->role != KVQ_ROLE_KEY && f->role != KVQ_ROLE_VALUE) return KVQ_ERR_UNSUPPORTED;
   if (f->granularity == KVQ_PER_TOKEN) return KVQ_OK;
+  if (f->granularity == KVQ_PER_TOKEN_GROUP) return f->group == 32 || f->group == 64 ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
   if (f->granularity != KVQ_PER_CHANNEL) return KVQ_ERR_UNSUPPORTED;
   if (f->role != KVQ_ROLE_KEY) return KVQ_ERR_UNSUPPORTED;
   if (f->group != 64 && f->group != 128) return KVQ_ERR_UNSUPPORTED;
@@ -255,7 +261,25 @@ int launch_pack(const uint16_t* x, int B, int H, int n, const kvq_format* f, int
                 uint32_t* codes, uint16_t* scale, uint16_t* zero, hipStream_t st) {
   const dim3 bh(1, (unsigned)(B * H));
   const SignBits sg = {{f->signs[0], f->signs[1], f->signs[2], f->signs[3]}};
-  if (f->granularity == KVQ_PER_TOKEN) {
+  if (f->granularity == KVQ_PER_TOKEN_GROUP) {
+    const dim3 grid((unsigned)(chunk_pad(n) / kTokenBlock), (unsigned)(B * H));
+    constexpr int T = 64 * D / 16;
+    if (f->role == KVQ_ROLE_KEY) {
+      if (f->group == 32)
+        pack_token_kernel<D, BITS, KVQ_ROLE_KEY, 32><<<grid, T, 0, st>>>(x, n, n_chunks, chunk_idx, f->hadamard, sg,
+                                                                         codes, scale, zero);
+      else
+        pack_token_kernel<D, BITS, KVQ_ROLE_KEY, 64><<<grid, T, 0, st>>>(x, n, n_chunks, chunk_idx, f->hadamard, sg,
+                                                                         codes, scale, zero);
+    } else {
+      if (f->group == 32)
+        pack_token_kernel<D, BITS, KVQ_ROLE_VALUE, 32><<<grid, T, 0, st>>>(x, n, n_chunks, chunk_idx, f->hadamard,
+                                                                           sg, codes, scale, zero);
+      else
+        pack_token_kernel<D, BITS, KVQ_ROLE_VALUE, 64><<<grid, T, 0, st>>>(x, n, n_chunks, chunk_idx, f->hadamard,
+                                                                           sg, codes, scale, zero);
+    }
+  } else if (f->granularity == KVQ_PER_TOKEN) {
     const dim3 grid((unsigned)(chunk_pad(n) / kTokenBlock), (unsigned)(B * H));
     if (f->role == KVQ_ROLE_KEY)
       pack_token_kernel<D, BITS, KVQ_ROLE_KEY><<<grid, 64 * D / 16, 0, st>>>(x, n, n_chunks, chunk_idx, f->hadamard,
@@ -294,6 +318,8 @@ extern "C" int kvq_window_elems(const kvq_format* fmt, int32_t B, int32_t H, int
   *code_words = bh * n_chunks * cp * d * fmt->bits / 32;
   if (fmt->granularity == KVQ_PER_TOKEN)
     *param_elems = bh * n_chunks * cp;
+  else if (fmt->granularity == KVQ_PER_TOKEN_GROUP)
+    *param_elems = bh * n_chunks * cp * (size_t)(fmt->group < d ? d / fmt->group : 1);
   else
     *param_elems = bh * n_chunks * (size_t)((chunk_len + fmt->group - 1) / fmt->group) * d;
   return KVQ_OK;
@@ -308,6 +334,7 @@ extern "C" int kvq_pack(const uint16_t* x, int32_t B, int32_t H, int32_t n, int3
   if (B < 1 || H < 1 || n < 1 || n_chunks < 1 || chunk_idx < 0 || chunk_idx >= n_chunks) return KVQ_ERR_SHAPE;
   if (d != 64 && d != 128) return KVQ_ERR_SHAPE;
   if (d == 64 && (fmt->signs[2] | fmt->signs[3])) return KVQ_ERR_UNSUPPORTED;
+  if (fmt->granularity == KVQ_PER_TOKEN_GROUP && fmt->group >= d) return KVQ_ERR_UNSUPPORTED;
   if ((long long)B * H > 65535) return KVQ_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scale) || !aligned16(zero)) return KVQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

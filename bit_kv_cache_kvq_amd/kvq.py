@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # KVQ_LIBRARY overrides the library file (development builds of kernel variants)
 library_path = os.environ.get("KVQ_LIBRARY") or os.path.join(_HERE, "libkvq.so")
 
-KVQ_PER_TOKEN, KVQ_PER_CHANNEL = 0, 1
+KVQ_PER_TOKEN, KVQ_PER_CHANNEL, KVQ_PER_TOKEN_GROUP = 0, 1, 2
 KVQ_ROLE_KEY, KVQ_ROLE_VALUE = 0, 1
 JB_CORR_NONE, JB_CORR_TAYLOR, JB_CORR_EXACT = 0, 1, 2
 
@@ -38,7 +38,8 @@ class KvqFormat(ctypes.Structure):
     @classmethod
     def make(cls, bits=2, granularity="token", group=128, hadamard=True, role="key", signs=None):
         """signs: None, or d values of +1/-1 (the randomized rotation H diag(s))."""
-        f = cls(bits, {"token": KVQ_PER_TOKEN, "channel": KVQ_PER_CHANNEL}[granularity], group,
+        gran = {"token": KVQ_PER_TOKEN, "channel": KVQ_PER_CHANNEL, "token_group": KVQ_PER_TOKEN_GROUP}[granularity]
+        f = cls(bits, gran, group,
                 int(bool(hadamard)), {"key": KVQ_ROLE_KEY, "value": KVQ_ROLE_VALUE}[role])
         for i, w in enumerate(sign_words(signs)):
             f.signs[i] = w
@@ -145,6 +146,8 @@ def window_shapes(fmt: KvqFormat, B: int, H: int, d: int, chunk_len: int, n_chun
         codes = (B, H, n_chunks * cp // 64, d, 64 // cpw)
     if fmt.granularity == KVQ_PER_TOKEN:
         params = (B, H, n_chunks * cp)
+    elif fmt.granularity == KVQ_PER_TOKEN_GROUP:
+        params = (B, H, n_chunks * cp, d // fmt.group)
     else:
         params = (B, H, n_chunks * (-(-chunk_len // fmt.group)), d)
     assert _prod(codes) == cw.value and _prod(params) == pe.value

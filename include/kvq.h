@@ -46,7 +46,7 @@ enum {
   KVQ_ERR_HIP = -6          /* the HIP launch failed */
 };
 
-enum { KVQ_PER_TOKEN = 0, KVQ_PER_CHANNEL = 1 };
+enum { KVQ_PER_TOKEN = 0, KVQ_PER_CHANNEL = 1, KVQ_PER_TOKEN_GROUP = 2 };
 enum { KVQ_ROLE_KEY = 0, KVQ_ROLE_VALUE = 1 };
 enum { JB_CORR_NONE = 0, JB_CORR_TAYLOR = 1, JB_CORR_EXACT = 2 };
 
@@ -64,6 +64,9 @@ enum { JB_CORR_NONE = 0, JB_CORR_TAYLOR = 1, JB_CORR_EXACT = 2 };
  *                  the block, token c*u + i in bits [bits*i, bits*i + bits).
  * Step size and zero point (fp16 bit patterns):
  *   KVQ_PER_TOKEN   [B, H, n_chunks*chunk_pad]
+ *   KVQ_PER_TOKEN_GROUP [B, H, n_chunks*chunk_pad, d/group]: §3's group-wise per-token
+ *                   granularity; pair j of a token covers channels [j*group, (j+1)*group)
+ *                   of the stored (rotated) basis; pad tokens hold 0.
  *   KVQ_PER_CHANNEL [B, H, n_chunks*ceil(chunk_len/group), d]; groups restart at each
  *                   chunk's first token, the last group of a chunk may be short.
  *
@@ -83,8 +86,10 @@ enum { JB_CORR_NONE = 0, JB_CORR_TAYLOR = 1, JB_CORR_EXACT = 2 };
  * the value format's. All-zero signs give R = H. */
 typedef struct {
   int32_t bits;        /* 2 or 4 */
-  int32_t granularity; /* KVQ_PER_TOKEN, or KVQ_PER_CHANNEL (role KEY only) */
-  int32_t group;       /* tokens per channel group: 64 or 128 (KVQ_PER_CHANNEL only) */
+  int32_t granularity; /* KVQ_PER_TOKEN, KVQ_PER_TOKEN_GROUP, or KVQ_PER_CHANNEL (role KEY only) */
+  int32_t group;       /* KVQ_PER_CHANNEL: tokens per channel group, 64 or 128;
+                          KVQ_PER_TOKEN_GROUP: channels per group, 32 or 64 (< d);
+                          ignored for KVQ_PER_TOKEN */
   int32_t hadamard;    /* 1: rotate by the normalized Sylvester-Hadamard matrix first */
   int32_t role;        /* KVQ_ROLE_KEY or KVQ_ROLE_VALUE: selects the code layout */
   uint32_t signs[4];   /* channel sign mask of a randomized rotation (hadamard = 1 only;

@@ -56,6 +56,10 @@ def test_geometry(kvq):
     assert kvq.window_shapes(f, 1, 40, 128, 4680, 8) == ((1, 40, 592, 128, 4), (1, 40, 37888))
     f = kvq.KvqFormat.make(4, "channel", 128, True, "key")
     assert kvq.window_shapes(f, 1, 40, 128, 4680, 8) == ((1, 40, 37888, 16), (1, 40, 296, 128))
+    f = kvq.KvqFormat.make(2, "token_group", 32, True, "value")
+    assert kvq.window_shapes(f, 1, 40, 128, 4680, 8) == ((1, 40, 592, 128, 4), (1, 40, 37888, 4))
+    f = kvq.KvqFormat.make(4, "token_group", 64, True, "key")
+    assert kvq.window_shapes(f, 2, 3, 128, 100, 2) == ((2, 3, 256, 16), (2, 3, 256, 2))
     # bytes per token and head at d=128: INT2 32 + 4, INT4 64 + 4 (codes + fp16 step and zero)
     assert 128 * 2 // 8 + 4 == 36 and 128 * 4 // 8 + 4 == 68
 
@@ -79,6 +83,8 @@ def test_pack_validation_without_launch(kvq):
     assert call(kvq.KvqFormat.make(3, "token", 128, True, "key"), p, 1, 1, 64, 128, 1, 0, p, p, p, None) == -3
     assert call(kvq.KvqFormat.make(2, "channel", 96, True, "key"), p, 1, 1, 64, 128, 1, 0, p, p, p, None) == -3
     assert call(kvq.KvqFormat.make(2, "channel", 128, True, "value"), p, 1, 1, 64, 128, 1, 0, p, p, p, None) == -3
+    assert call(kvq.KvqFormat.make(2, "token_group", 16, True, "key"), p, 1, 1, 64, 128, 1, 0, p, p, p, None) == -3
+    assert call(kvq.KvqFormat.make(2, "token_group", 64, True, "key"), p, 1, 1, 64, 64, 1, 0, p, p, p, None) == -3
     q = ctypes.c_void_p(18)
     assert call(f, q, 1, 1, 64, 128, 1, 0, p, p, p, None) == -4              # misaligned
     nosign = kvq.KvqFormat.make(2, "token", 128, False, "key", [-1] + [1] * 127)

@@ -112,3 +112,17 @@ def test_pack_randomized_rotation(d, bits, gran, role):
     x = synth.draw(w, "k_cache")
     s = synth.draw_signs(d, 5, "k")
     _check_window(x, w.chunk_len, bits, gran, 128, 1, role, None, f"signs d{d}", signs=s)
+
+
+@pytest.mark.parametrize("g", [32, 64])
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("role", ["key", "value"])
+def test_pack_token_group(g, bits, role):
+    # group-wise per token (channel groups of g, one step and zero point each), on a ragged
+    # chunk length, with the degenerate-range and outlier rows of the edge input
+    x = _edge_input(3 * 97, 128, 31 + g + bits)
+    _check_window(x, 97, bits, "token_group", g, 1, role, label=f"token_group g={g}")
+    _check_window(x[..., :64], 97, bits, "token_group", 32, 0, role, label=f"token_group d=64 g=32")
+    w = synth.WORKLOADS["c24"]
+    xc = synth.draw(w, "k_cache" if role == "key" else "v_cache", heads=[(0, 0), (0, 23)])[None]
+    _check_window(xc, w.chunk_len, bits, "token_group", g, 1, role, label=f"c24 heads token_group g={g}")

@@ -58,7 +58,7 @@ def window_memory(w):
     from bit_kv_cache_kvq_amd import kvq, window
     def kv(bits):
         kf = kvq.KvqFormat.make(bits, w.k_granularity, w.group, True, "key")
-        vf = kvq.KvqFormat.make(bits, "token", w.group, True, "value")
+        vf = kvq.KvqFormat.make(bits, w.v_granularity, w.group, True, "value")
         return sum(window.window_bytes(f, w.B, w.H, w.d, w.chunk_len, w.n_chunks) for f in (kf, vf))
     b2, b4, b16 = kv(2), kv(4), 2 * w.B * w.H * w.n_chunks * w.chunk_len * w.d * 2
     return {"int2_bytes": b2, "int4_bytes": b4, "bf16_bytes": b16, "int2_over_int4": round(b2 / b4, 4),
@@ -148,7 +148,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
 
     kf = kvq.KvqFormat.make(w.bits, w.k_granularity, w.group, True, "key")
-    vf = kvq.KvqFormat.make(w.bits, "token", w.group, True, "value")
+    vf = kvq.KvqFormat.make(w.bits, w.v_granularity, w.group, True, "value")
     if not 1 <= args.layers <= kvq.KVQ_BATCH_MAX:
         print(f"--layers must be in 1..{kvq.KVQ_BATCH_MAX}", file=sys.stderr)
         sys.exit(2)
@@ -259,7 +259,7 @@ def main():
         heads = [(0, h) for h in range(min(args.cpu_heads, w.bh))] if w.B == 1 else \
             [(b, h) for b in range(w.B) for h in range(w.H)][: args.cpu_heads]
         kf_o = Format(w.bits, w.k_granularity, w.group, True, "key")
-        vf_o = Format(w.bits, "token", w.group, True, "value")
+        vf_o = Format(w.bits, w.v_granularity, w.group, True, "value")
         base, (O, PS, PR) = cpu_baseline(w, x, heads, kf_o, vf_o, CORR_NAMES[args.correction])
         og = np.stack([o[b, h].cpu().numpy() for (b, h) in heads])[None]
         rms = np.sqrt((O ** 2).mean())

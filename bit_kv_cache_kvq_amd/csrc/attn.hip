@@ -205,16 +205,29 @@ struct SmemSlots {
     uint32_t zv[kBN / 2];   // (-1024 - z^V) fp16 pairs, token pair (j, j+8) order
     uint32_t dvp[kBN / 2];  // (Delta^V_j, Delta^V_j+8) fp16 pairs
   };
+  // Group-wise keys and values (NG channel groups per token): bias operand slots 16..31,
+  // and one zero-point / step pair table per value channel group.
+  struct PSlotG : PSlot {
+    uint4 kb2[kBN][2];
+  };
+  template <int NG>
+  struct ZSlotG {
+    uint32_t zv[NG][kBN / 2];
+    uint32_t dvp[NG][kBN / 2];
+  };
 };
 
-// The LDS of a workgroup: a three-slot ring of key, value and parameter tiles.
-template <int D, bool PERCH = false>
+// The LDS of a workgroup: a three-slot ring of key, value and parameter tiles (TG > 0:
+// keys and values quantized in groups of TG channels per token).
+template <int D, bool PERCH = false, int TG = 0>
 struct Smem : SmemSlots<D> {
   using T = SmemSlots<D>;
+  using PS = std::conditional_t<(TG > 0), typename T::PSlotG, typename T::PSlot>;
+  using ZS = std::conditional_t<(TG > 0), typename T::template ZSlotG<(TG > 0 ? D / TG : 1)>, typename T::ZSlot>;
   alignas(16) typename T::KSlot k[3];
   alignas(16) _Float16 v[3][D][T::VROW];  // value rows: fp16((code - z) Delta^V) or current values
-  alignas(16) typename T::PSlot prm[3];
-  alignas(16) typename T::ZSlot z[3];
+  alignas(16) PS prm[3];
+  alignas(16) ZS z[3];
   alignas(16) float a_stream[kNS];
 };
 
@@ -223,7 +236,7 @@ struct Smem : SmemSlots<D> {
 // by the query index against bank conflicts), behind three packed code slots; the current
 // chunk's key slots overlay both.
 template <int D>
-struct Smem<D, true> : SmemSlots<D> {
+struct Smem<D, true, 0> : SmemSlots<D> {
   using T = SmemSlots<D>;
   union {
     typename T::KSlot k[3];
@@ -248,10 +261,19 @@ using Kind = std::integral_constant<int, K>;
 // One workgroup's work: workgroup wg of the n_wg a call launches (n_qblk * B * H *
 // n_split; the linear ids are dealt to the XCDs round-robin, wg % 8 being the XCD). The
 // LDS is declared here rather than passed in: the kernels address it as before.
-template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT, int TG = 0>
 __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_wg) {
-  __shared__ Smem<D, PERCH> sm;
-  using SM = Smem<D, PERCH>;
+  __shared__ Smem<D, PERCH, TG> sm;
+  using SM = Smem<D, PERCH, TG>;
+  // Group-wise keys and values (TG channels per group): NG (step, zero point) pairs per
+  // token; K-step kk of the int8 QK^T covers channels [32 kk, 32 kk + 32), so a group is
+  // KPG whole K-steps. The bias MFMA carries 3 fp16 slots (hi/lo cross terms) per group
+  // for the zero point and per group for the correction, plus -m and the mask: a second
+  // bias MFMA (slots 16..31) when that passes 16.
+  constexpr int NG = TG > 0 ? D / TG : 1;
+  constexpr int KPG = TG > 0 ? TG / 32 : 1;
+  constexpr int NB = (TG > 0 && 6 * NG + 3 > 16) ? 2 : 1;
+  static_assert(TG == 0 || (!PERCH && !EXACT && TG % 32 == 0 && TG < D && NG <= kNS), "group-wise options");
   constexpr int HALF = D / 2;
   constexpr int KSTEPS = D / 32;  // int8 K-steps of 32 channels
   constexpr int CBLK = D / 32;    // 32-channel output blocks
@@ -295,6 +317,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // ---------------- query operands ----------------
   i32x4 qhi[KSTEPS], qlo[KSTEPS];  // int8 hi/lo of q_f (cached keys), or the bf16 query
   f16x8 qbias;                     // query operand of the bias MFMA
+  f16x8 qbias2 = {};               // group-wise keys: the second bias MFMA's (slots 16..31)
   float m_run = -INFINITY;         // reference max (log2 units); -inf until the first block
   float a_st = 0.f;                // A of this wave's stream
   // Rotated query q' = H q / sqrt(d) (or q) of this lane's half: channels HALF h + i.
@@ -349,6 +372,21 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   auto build_query = [&]() KVQ_INLINE {
     float qv[HALF];
     rotated_query(qv);
+    if constexpr (TG > 0) {
+      // slot (kk, i) of half h takes channel 32 kk + 16 h + i (both halves' channels of a
+      // 32-channel block sit in one half of the rotation's layout: one exchange moves them)
+      float qn[HALF];
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; kk++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int c0 = 32 * kk + i, c1 = c0 + 16, o = c0 / HALF;
+          const float recv = xor32(qv[(o == 0 ? c1 : c0) % HALF]);
+          qn[16 * kk + i] = h == o ? qv[(o == 0 ? c0 : c1) % HALF] : recv;
+        }
+#pragma unroll
+      for (int i = 0; i < HALF; i++) qv[i] = qn[i];
+    }
     float ss = 0.f, mxa = 0.f;
 #pragma unroll
     for (int i = 0; i < HALF; i++) {
@@ -361,6 +399,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
     const float A = mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
     int qs = 0;
+    int qsg[NG] = {};  // group-wise keys: this half's sum of q_f over each group
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; kk++)
 #pragma unroll
@@ -372,6 +411,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           const int hi = (qf + 128) >> 8;
           const int lo = qf - (hi << 8);
           qs += qf;
+          if constexpr (TG > 0) qsg[kk / KPG] += qf;
           whi |= (uint32_t)(hi & 0xFF) << (8 * b);
           wlo |= (uint32_t)(lo & 0xFF) << (8 * b);
         }
@@ -419,6 +459,41 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
 #pragma unroll
       for (int e = 3; e < 8; e++) qbias[e] = (_Float16)0.f;
     }
+    if constexpr (TG > 0) {
+      // term t: zero point of group t (t < NG), correction of group t - NG; its three
+      // slots are k = 3t .. 3t+2 at bias slot k + 3 (k >= 8): 8, 9, 10 carry -m and the mask
+      _Float16 qsl[16 * NB];
+#pragma unroll
+      for (int k = 0; k < 16 * NB; k++) qsl[k] = (_Float16)0.f;
+#pragma unroll
+      for (int t = 0; t < 2 * NG; t++) {
+        float y;
+        if (t < NG) {
+          y = -A * (float)(qsg[t] + __shfl_xor(qsg[t], 32));
+        } else {
+          float sg = 0.f;
+#pragma unroll
+          for (int kk = (t - NG) * KPG; kk < (t - NG + 1) * KPG; kk++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) sg += qv[16 * kk + i] * qv[16 * kk + i];
+          sg += xor32(sg);
+          y = p.correction ? -(p.s * p.s * sg * (1.f / 24.f) * kLog2e) * kD2Scale : 0.f;
+        }
+        _Float16 yh, yl;
+        split16(y, yh, yl);
+        const int k0 = 3 * t;
+        qsl[k0 + (k0 >= 8 ? 3 : 0)] = yh;
+        qsl[k0 + 1 + (k0 + 1 >= 8 ? 3 : 0)] = yl;
+        qsl[k0 + 2 + (k0 + 2 >= 8 ? 3 : 0)] = yh;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e++) qbias[e] = h ? qsl[8 + e] : qsl[e];
+      if (h) qbias[2] = (_Float16)(-kMaskLogit);
+      if constexpr (NB == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) qbias2[e] = h ? qsl[24 + e] : qsl[16 + e];
+      }
+    }
     write_mslot();  // -m (hi, lo); 0 while m is unset
     if (lane == 0) sm.a_stream[wave] = A;
     __syncthreads();
@@ -460,19 +535,20 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   const size_t n_str = (size_t)p.n_wchunks * p.cp;    // per-head stride of the window arrays
   const uint32_t* kc_base = p.k_codes + (size_t)bh * n_str * KW;
   const uint32_t* vc_base = p.v_codes + (size_t)bh * (n_str / kBN) * VWT;
-  const uint16_t* ks_base = p.k_scale + (size_t)bh * n_str;
-  const uint16_t* kz_base = p.k_zero + (size_t)bh * n_str;
-  const uint16_t* vs_base = p.v_scale + (size_t)bh * n_str;
-  const uint16_t* vz_base = p.v_zero + (size_t)bh * n_str;
+  constexpr int PPT = TG > 0 ? NG : 1;  // (step, zero point) pairs per token
+  const uint16_t* ks_base = p.k_scale + (size_t)bh * n_str * PPT;
+  const uint16_t* kz_base = p.k_zero + (size_t)bh * n_str * PPT;
+  const uint16_t* vs_base = p.v_scale + (size_t)bh * n_str * PPT;
+  const uint16_t* vz_base = p.v_zero + (size_t)bh * n_str * PPT;
   const uint16_t* kr_base = p.k_cur + (size_t)bh * p.n_r * D;
   const uint16_t* vr_base = p.v_cur + (size_t)bh * p.n_r * D;
   // descriptors of this head's cached window (the byte sizes fit 31 bits: checked on the host)
   const __amdgpu_buffer_rsrc_t rs_kc = buffer_rsrc(kc_base, (uint32_t)(n_tot * KW * 4));
   const __amdgpu_buffer_rsrc_t rs_vc = buffer_rsrc(vc_base, (uint32_t)(n_tot * VWT / kBN * 4));
-  const __amdgpu_buffer_rsrc_t rs_ks = buffer_rsrc(ks_base, (uint32_t)(n_tot * 2));
-  const __amdgpu_buffer_rsrc_t rs_kz = buffer_rsrc(kz_base, (uint32_t)(n_tot * 2));
-  const __amdgpu_buffer_rsrc_t rs_vs = buffer_rsrc(vs_base, (uint32_t)(n_tot * 2));
-  const __amdgpu_buffer_rsrc_t rs_vz = buffer_rsrc(vz_base, (uint32_t)(n_tot * 2));
+  const __amdgpu_buffer_rsrc_t rs_ks = buffer_rsrc(ks_base, (uint32_t)(n_tot * 2 * PPT));
+  const __amdgpu_buffer_rsrc_t rs_kz = buffer_rsrc(kz_base, (uint32_t)(n_tot * 2 * PPT));
+  const __amdgpu_buffer_rsrc_t rs_vs = buffer_rsrc(vs_base, (uint32_t)(n_tot * 2 * PPT));
+  const __amdgpu_buffer_rsrc_t rs_vz = buffer_rsrc(vz_base, (uint32_t)(n_tot * 2 * PPT));
   auto n_valid = [&](int U) KVQ_INLINE {
     return U < n_ct ? min(kBN, p.chunk_len - (U % tiles_per_chunk) * kBN) : min(kBN, p.n_r - (U - n_ct) * kBN);
   };
@@ -617,6 +693,20 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   uint32_t pk_dk = 0, pk_zk = 0;                 // key step / zero point of key tid & 63
   uint4 gpre = make_uint4(0, 0, 0, 0);           // per-channel keys: 16 bytes of the group rows
   uint32_t pz0 = 0, pz1 = 0, pd0 = 0, pd1 = 0;   // value zero points / steps of a token pair
+  // group-wise: the NG fp16 pairs of a token (groups 0, 1 in .x, groups 2, 3 in .y)
+  uint2 gk_d = make_uint2(0, 0), gk_z = make_uint2(0, 0);
+  uint2 gv_z0 = make_uint2(0, 0), gv_z1 = make_uint2(0, 0), gv_d0 = make_uint2(0, 0), gv_d1 = make_uint2(0, 0);
+  auto load_pairs = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t tok, uint32_t tok0) KVQ_INLINE -> uint2 {
+    if constexpr (NG == 4) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rs, tok * 8u, tok0 * 8u, 0);
+      return make_uint2(w[0], w[1]);
+    } else {
+      return make_uint2(__builtin_amdgcn_raw_buffer_load_b32(rs, tok * 4u, tok0 * 4u, 0), 0u);
+    }
+  };
+  auto pair_bits = [&](const uint2& w, int g) KVQ_INLINE -> uint32_t {
+    return ((g < 2 ? w.x : w.y) >> (16 * (g & 1))) & 0xFFFFu;
+  };
 
   auto load_k = [&](int U, auto k_c) KVQ_INLINE {
     if constexpr (decltype(k_c)::value == kCached) {
@@ -633,7 +723,11 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           kpre[i].x = __builtin_amdgcn_raw_buffer_load_b32(rs_kc, un * 4u, tok0 * KW * 4u, 0);
         }
       }
-      if constexpr (!PERCH) {
+      if constexpr (TG > 0) {
+        const uint32_t j = (uint32_t)(tid & (kBN - 1));
+        gk_d = load_pairs(rs_ks, j, tok0);
+        gk_z = load_pairs(rs_kz, j, tok0);
+      } else if constexpr (!PERCH) {
         const uint32_t j = (uint32_t)(tid & (kBN - 1));
         pk_dk = __builtin_amdgcn_raw_buffer_load_b16(rs_ks, j * 2u, tok0 * 2u, 0);
         pk_zk = __builtin_amdgcn_raw_buffer_load_b16(rs_kz, j * 2u, tok0 * 2u, 0);
@@ -645,7 +739,13 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         const uint16_t* src = tid < D / 8 ? p.k_scale : p.k_zero;
         gpre = reinterpret_cast<const uint4*>(src + row)[tid % (D / 8)];
       }
-      if constexpr (!MASS_ONLY) {
+      if constexpr (!MASS_ONLY && TG > 0) {
+        const uint32_t j = (uint32_t)(16 * ((tid >> 3) & 3) + (tid & 7));
+        gv_z0 = load_pairs(rs_vz, j, tok0);
+        gv_z1 = load_pairs(rs_vz, j + 8u, tok0);
+        gv_d0 = load_pairs(rs_vs, j, tok0);
+        gv_d1 = load_pairs(rs_vs, j + 8u, tok0);
+      } else if constexpr (!MASS_ONLY) {
         const uint32_t j = (uint32_t)(16 * ((tid >> 3) & 3) + (tid & 7));
         pz0 = __builtin_amdgcn_raw_buffer_load_b16(rs_vz, j * 2u, tok0 * 2u, 0);
         pz1 = __builtin_amdgcn_raw_buffer_load_b16(rs_vz, j * 2u + 16u, tok0 * 2u, 0);
@@ -664,7 +764,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   };
   auto store_k = [&](int U, int slot, auto k_c) KVQ_INLINE {
     typename SM::KSlot& ks = sm.k[slot];
-    typename SM::PSlot& ps = sm.prm[slot];
+    auto& ps = sm.prm[slot];
     const int nv = n_valid(U);
     if constexpr (decltype(k_c)::value == kCached) {
 #pragma unroll
@@ -689,7 +789,13 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       if constexpr (PERCH) {
         if (tid < D / 4) reinterpret_cast<uint4*>(&ps.dka[0][0])[tid] = gpre;
       }
-      if constexpr (!PERCH) {
+      if constexpr (TG > 0) {
+        // per-group steps Delta_jg (0 for padding keys), one row per group, M-row order
+        if (wave < NG) {
+          const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
+          ps.dka[wave][r] = lane < nv ? half_bits_to_f32(pair_bits(gk_d, wave)) : 0.f;
+        }
+      } else if constexpr (!PERCH) {
         const int key = tid & (kBN - 1);
         const int r = 32 * (key >> 5) + key_mrow(key & 31);
         const float dk = key < nv ? half_bits_to_f32(pk_dk) : 0.f;
@@ -699,7 +805,44 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           ps.d4[r] = (dk * dk) * (dk * dk);
         }
       }
-      if (PERCH && wave == 0) {
+      if constexpr (TG > 0) {
+        if (wave == 0) {
+          // bias key operand: term t (zero point Delta z of group t, then Delta^2 / 64 of
+          // group t - NG) as (hi, hi, lo) at slots k = 3t.., slot k + 3 from k = 8 on;
+          // slots 8, 9 = 1 (the -m pair), 10 = the mask
+          const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
+          uint32_t ksl[8 * NB];
+#pragma unroll
+          for (int k = 0; k < 8 * NB; k++) ksl[k] = 0u;
+          const uint32_t one = 0x3C00u;
+          ksl[4] = one | (one << 16);
+          if (lane < nv) {
+#pragma unroll
+            for (int t = 0; t < 2 * NG; t++) {
+              const int g = t < NG ? t : t - NG;
+              const float dk = half_bits_to_f32(pair_bits(gk_d, g));
+              const float x = t < NG ? dk * half_bits_to_f32(pair_bits(gk_z, g)) : dk * dk * (1.f / kD2Scale);
+              _Float16 xh, xl;
+              split16(x, xh, xl);
+              const uint32_t hb = __builtin_bit_cast(uint16_t, xh), lb = __builtin_bit_cast(uint16_t, xl);
+              const uint32_t v3[3] = {hb, hb, lb};
+#pragma unroll
+              for (int e = 0; e < 3; e++) {
+                const int k = 3 * t + e, sl = k + (k >= 8 ? 3 : 0);
+                ksl[sl >> 1] |= v3[e] << (16 * (sl & 1));
+              }
+            }
+          } else {
+            ksl[5] = one;  // the mask slot: padding keys get -65504
+          }
+          ps.kb[r][0] = make_uint4(ksl[0], ksl[1], ksl[2], ksl[3]);
+          ps.kb[r][1] = make_uint4(ksl[4], ksl[5], ksl[6], ksl[7]);
+          if constexpr (NB == 2) {
+            ps.kb2[r][0] = make_uint4(ksl[8], ksl[9], ksl[10], ksl[11]);
+            ps.kb2[r][1] = make_uint4(ksl[12], ksl[13], ksl[14], ksl[15]);
+          }
+        }
+      } else if (PERCH && wave == 0) {
         // per-channel keys: the group terms ride on the query side (slots 8, 9)
         const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
         ps.kb[r][0] = make_uint4(0, 0, 0, 0);
@@ -720,9 +863,21 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         }
         ps.kb[r][0] = row;
       }
-      if constexpr (!MASS_ONLY) {
+      if constexpr (!MASS_ONLY && TG > 0) {
         if (wave == 2 && lane < kBN / 2) {
-          typename SM::ZSlot& zs = sm.z[slot];
+          auto& zs = sm.z[slot];
+          const int g = lane >> 3, j = lane & 7;
+          const bool ok0 = 16 * g + j < nv, ok1 = 16 * g + j + 8 < nv;
+#pragma unroll
+          for (int gg = 0; gg < NG; gg++) {
+            zs.zv[gg][lane] = pack_f16x2(ok0 ? -1024.f - half_bits_to_f32(pair_bits(gv_z0, gg)) : -1024.f,
+                                         ok1 ? -1024.f - half_bits_to_f32(pair_bits(gv_z1, gg)) : -1024.f);
+            zs.dvp[gg][lane] = (ok0 ? pair_bits(gv_d0, gg) : 0u) | ((ok1 ? pair_bits(gv_d1, gg) : 0u) << 16);
+          }
+        }
+      } else if constexpr (!MASS_ONLY) {
+        if (wave == 2 && lane < kBN / 2) {
+          auto& zs = sm.z[slot];
           const int g = lane >> 3, j = lane & 7;
           const bool ok0 = 16 * g + j < nv, ok1 = 16 * g + j + 8 < nv;
           zs.zv[lane] = pack_f16x2(ok0 ? -1024.f - half_bits_to_f32(pz0) : -1024.f,
@@ -744,7 +899,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         ps.kb[r][0] = make_uint4(0, 0, 0, 0);
       }
     }
-    if (wave == 1) {
+    if (wave == 1 && !(TG > 0 && decltype(k_c)::value == kCached)) {
       // bias key operand, slots 8..15: 1, 1, mask, 0...
       const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
       const uint32_t one = 0x3C00u;
@@ -787,20 +942,25 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     _Float16(*vrows)[SM::VROW] = sm.v[slot];
     if constexpr (decltype(k_c)::value == kCached) {
       if (tid >= kVST) return;
-      const typename SM::ZSlot& zs = sm.z[slot];
+      const auto& zs = sm.z[slot];
       // every group of this lane has the same token group g = tid mod 4 (kVST % 4 == 0)
       const int g = tid & 3;
-      const uint4 z0 = *reinterpret_cast<const uint4*>(&zs.zv[8 * g]);
-      const uint4 z1 = *reinterpret_cast<const uint4*>(&zs.zv[8 * g + 4]);
-      const uint4 d0 = *reinterpret_cast<const uint4*>(&zs.dvp[8 * g]);
-      const uint4 d1 = *reinterpret_cast<const uint4*>(&zs.dvp[8 * g + 4]);
-      const uint32_t zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-      const uint32_t dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+      auto zd_rows = [&](const uint32_t* zrow, const uint32_t* drow, uint32_t* zz, uint32_t* dd) KVQ_INLINE {
+        const uint4 z0 = *reinterpret_cast<const uint4*>(&zrow[8 * g]);
+        const uint4 z1 = *reinterpret_cast<const uint4*>(&zrow[8 * g + 4]);
+        const uint4 d0 = *reinterpret_cast<const uint4*>(&drow[8 * g]);
+        const uint4 d1 = *reinterpret_cast<const uint4*>(&drow[8 * g + 4]);
+        zz[0] = z0.x, zz[1] = z0.y, zz[2] = z0.z, zz[3] = z0.w, zz[4] = z1.x, zz[5] = z1.y, zz[6] = z1.z, zz[7] = z1.w;
+        dd[0] = d0.x, dd[1] = d0.y, dd[2] = d0.z, dd[3] = d0.w, dd[4] = d1.x, dd[5] = d1.y, dd[6] = d1.z, dd[7] = d1.w;
+      };
+      uint32_t zz[8], dd[8];
+      if constexpr (TG == 0) zd_rows(zs.zv, zs.dvp, zz, dd);
 #pragma unroll
       for (int i = 0; i < VGPT; i++) {
         const int vg = tid + i * kVST;
         if (VGROUPS % kVST != 0 && vg >= VGROUPS) break;
         const int ch = vg >> 2;  // 16-token group g of channel ch
+        if constexpr (TG > 0) zd_rows(zs.zv[ch / TG], zs.dvp[ch / TG], zz, dd);
         uint32_t a[8];
         if constexpr (BITS == 2) {
           const uint32_t w = vpre[i].x;
@@ -866,16 +1026,24 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
 
   // Key-side operands of block mb of tile U: the bias row and the key codes (cached) or
   // bf16 key rows (current), read from LDS ahead of their MFMAs.
-  uint4 kbop;
+  uint4 kbop, kbop2 = make_uint4(0, 0, 0, 0);
   i32x4 kop[D / 16];
+  int rk_slot = 0, rk_mb = 0;  // group-wise keys: the block whose operands read_k loaded
   auto read_k = [&](int slot, int mb, auto k_c) KVQ_INLINE {
     const typename SM::KSlot& ks = sm.k[slot];
     const int krow = 32 * mb + mrow_key(col);
     kbop = sm.prm[slot].kb[32 * mb + col][h];
     if constexpr (decltype(k_c)::value == kCached) {
+      if constexpr (TG > 0) {
+        rk_slot = slot;
+        rk_mb = mb;
+        if constexpr (NB == 2) kbop2 = sm.prm[slot].kb2[32 * mb + col][h];
+      }
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; kk++) {
-        if constexpr (PERCH)
+        if constexpr (TG > 0)  // K-step kk: channels 32 kk + 16 h ..
+          kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][32 * kk + 16 * h]);
+        else if constexpr (PERCH)
           kop[kk] = *reinterpret_cast<const i32x4*>(&sm.kc(slot)[krow][HALF * h + 16 * kk]);
         else
           kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
@@ -892,7 +1060,34 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       const f32x16 zf = {};
       cb[SET] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kbop), qbias, zf, 0, 0, 0);
     }
-    if constexpr (decltype(k_c)::value == kCached) {
+    if constexpr (decltype(k_c)::value == kCached && NB == 2) {
+      cb[SET] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kbop2), qbias2, cb[SET], 0, 0, 0);
+    }
+    if constexpr (decltype(k_c)::value == kCached && TG > 0) {
+      // one exact int32 sum per channel group, scaled by the key's step of that group
+      const float* dkg = &sm.prm[rk_slot].dka[0][0];
+      f32x16 sf = {};
+#pragma unroll
+      for (int gq = 0; gq < NG; gq++) {
+        i32x16 a = {};
+#pragma unroll
+        for (int k2 = 0; k2 < KPG; k2++)
+          a = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[gq * KPG + k2], qhi[gq * KPG + k2], a, 0, 0, 0);
+        a = a << 8;
+#pragma unroll
+        for (int k2 = 0; k2 < KPG; k2++)
+          a = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[gq * KPG + k2], qlo[gq * KPG + k2], a, 0, 0, 0);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; v4++) {
+          const float4 d4 = *reinterpret_cast<const float4*>(&dkg[gq * kBN + 32 * rk_mb + 8 * v4 + 4 * h]);
+          sf[4 * v4 + 0] = fmaf(d4.x, (float)a[4 * v4 + 0], sf[4 * v4 + 0]);
+          sf[4 * v4 + 1] = fmaf(d4.y, (float)a[4 * v4 + 1], sf[4 * v4 + 1]);
+          sf[4 * v4 + 2] = fmaf(d4.z, (float)a[4 * v4 + 2], sf[4 * v4 + 2]);
+          sf[4 * v4 + 3] = fmaf(d4.w, (float)a[4 * v4 + 3], sf[4 * v4 + 3]);
+        }
+      }
+      sqh[SET] = __builtin_bit_cast(i32x16, sf);
+    } else if constexpr (decltype(k_c)::value == kCached) {
       // S = 256 S_hi + S_lo in one accumulator: the hi sums, a shift, then the lo sums
       i32x16 acc_s = {};
 #pragma unroll
@@ -943,7 +1138,10 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // Logits (log2 units; they carry -m through the bias) of block mb of tile U from SET.
   auto logits = [&](int slot, int mb, auto set_c, auto k_c, float* x) KVQ_INLINE {
     constexpr int SET = decltype(set_c)::value;
-    if constexpr (decltype(k_c)::value == kCached && PERCH) {
+    if constexpr (decltype(k_c)::value == kCached && TG > 0) {
+#pragma unroll
+      for (int v = 0; v < 16; v++) x[v] = fmaf(a_st, __int_as_float(sqh[SET][v]), cb[SET][v]);
+    } else if constexpr (decltype(k_c)::value == kCached && PERCH) {
 #pragma unroll
       for (int v = 0; v < 16; v++) x[v] = fmaf(a_ch, (float)sqh[SET][v], cb[SET][v]);
     } else if constexpr (decltype(k_c)::value == kCached) {
@@ -1223,9 +1421,9 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   }
 }
 
-template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT, int TG = 0>
 __global__ __launch_bounds__(kThreads) void jb_attn_kernel(const Params p) {
-  attn_body<D, BITS, MASS_ONLY, PERCH, EXACT>(p, blockIdx.x, gridDim.x);
+  attn_body<D, BITS, MASS_ONLY, PERCH, EXACT, TG>(p, blockIdx.x, gridDim.x);
 }
 
 // Several calls in one launch: call c owns workgroups start[c] .. start[c] + grid[c] - 1.
@@ -1821,8 +2019,15 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   if (kf.bits != 2 && kf.bits != 4) return KVQ_ERR_UNSUPPORTED;
   if (vf.bits != kf.bits) return KVQ_ERR_UNSUPPORTED;
   if (kf.role != KVQ_ROLE_KEY || vf.role != KVQ_ROLE_VALUE) return KVQ_ERR_UNSUPPORTED;
-  if (vf.granularity != KVQ_PER_TOKEN) return KVQ_ERR_UNSUPPORTED;
-  if (kf.granularity != KVQ_PER_TOKEN && kf.granularity != KVQ_PER_CHANNEL) return KVQ_ERR_UNSUPPORTED;
+  if (kf.granularity == KVQ_PER_TOKEN_GROUP || vf.granularity == KVQ_PER_TOKEN_GROUP) {
+    // group-wise keys and values together, one group size, second-order correction
+    if (kf.granularity != vf.granularity || kf.group != vf.group) return KVQ_ERR_UNSUPPORTED;
+    if ((kf.group != 32 && kf.group != 64) || kf.group >= a->d) return KVQ_ERR_UNSUPPORTED;
+    if (a->correction == JB_CORR_EXACT) return KVQ_ERR_UNSUPPORTED;
+  } else {
+    if (vf.granularity != KVQ_PER_TOKEN) return KVQ_ERR_UNSUPPORTED;
+    if (kf.granularity != KVQ_PER_TOKEN && kf.granularity != KVQ_PER_CHANNEL) return KVQ_ERR_UNSUPPORTED;
+  }
   if (kf.granularity == KVQ_PER_CHANNEL && kf.group != 64 && kf.group != 128) return KVQ_ERR_UNSUPPORTED;
   if ((kf.hadamard | vf.hadamard) & ~1) return KVQ_ERR_UNSUPPORTED;
   for (const kvq_format* f : {&kf, &vf}) {
@@ -2076,11 +2281,11 @@ Params fill_params(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   return p;
 }
 
-template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT = false>
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT = false, int TG = 0>
 int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
   const Params p = fill_params<D, MASS_ONLY, PERCH>(a, pl, st);
   const unsigned grid = (unsigned)(pl.n_qblk * a->B * a->H * pl.n_split);
-  jb_attn_kernel<D, BITS, MASS_ONLY, PERCH, EXACT><<<grid, kThreads, 0, st>>>(p);
+  jb_attn_kernel<D, BITS, MASS_ONLY, PERCH, EXACT, TG><<<grid, kThreads, 0, st>>>(p);
   if (pl.n_split > 1) {
     const size_t rows = (size_t)a->B * a->H * a->n_q;
     constexpr int G = MASS_ONLY ? 1 : D / 4;
@@ -2129,6 +2334,17 @@ int dispatch(const jb_attn_args* a, void* stream) {
   if (pl.n_split > 1 && !aligned16(a->workspace)) return KVQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool perch = a->k_fmt.granularity == KVQ_PER_CHANNEL;
+  if (a->k_fmt.granularity == KVQ_PER_TOKEN_GROUP) {
+    const bool i2 = a->k_fmt.bits == 2;
+    if (a->d == 64)
+      return i2 ? launch_attn<64, 2, MASS_ONLY, false, false, 32>(a, pl, s)
+                : launch_attn<64, 4, MASS_ONLY, false, false, 32>(a, pl, s);
+    if (a->k_fmt.group == 32)
+      return i2 ? launch_attn<128, 2, MASS_ONLY, false, false, 32>(a, pl, s)
+                : launch_attn<128, 4, MASS_ONLY, false, false, 32>(a, pl, s);
+    return i2 ? launch_attn<128, 2, MASS_ONLY, false, false, 64>(a, pl, s)
+              : launch_attn<128, 4, MASS_ONLY, false, false, 64>(a, pl, s);
+  }
   if (a->correction == JB_CORR_EXACT && a->n_chunks > 0) {
     if (a->d == 128) {
       if (a->k_fmt.bits == 2)
@@ -2210,6 +2426,7 @@ int dispatch_batch(const jb_attn_args* calls, int n, void* stream) {
     const int st = validate_attn(&calls[c], MASS_ONLY);
     if (st) return st;
     const jb_attn_args& a = calls[c];
+    if (a.k_fmt.granularity == KVQ_PER_TOKEN_GROUP) return KVQ_ERR_UNSUPPORTED;  // single calls only
     if (a.d != a0.d || a.k_fmt.bits != a0.k_fmt.bits || a.k_fmt.granularity != a0.k_fmt.granularity ||
         (a.k_fmt.granularity == KVQ_PER_CHANNEL && a.k_fmt.group != a0.k_fmt.group) ||
         (a.correction == JB_CORR_EXACT) != (a0.correction == JB_CORR_EXACT))

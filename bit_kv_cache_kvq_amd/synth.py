@@ -51,11 +51,16 @@ class Workload:
     k_dist: str = "outlier"   # "outlier": N(0,1) with scaled channels; "t3": Student-t(3)
     n_outlier: int = 4
     outlier_scale: float = 10.0
-    k_granularity: str = "token"  # "token" | "channel"
-    group: int = 128              # tokens per per-channel key group
+    k_granularity: str = "token"  # "token" | "channel" | "token_group"
+    group: int = 128              # tokens per per-channel key group, or channels per token group
     bits: int = 2
     masses: bool = False
     seed: int = 0
+
+    @property
+    def v_granularity(self) -> str:
+        """Values are per token, or group-wise per token together with group-wise keys."""
+        return "token_group" if self.k_granularity == "token_group" else "token"
 
     @property
     def n_r(self) -> int:
@@ -88,6 +93,9 @@ WORKLOADS = {
     "c40": Workload("c40", B=1, H=40, d=128, n_q=4680, chunk_len=4680, n_chunks=8),
     "c40_perch": Workload("c40_perch", B=1, H=40, d=128, n_q=4680, chunk_len=4680, n_chunks=8,
                           k_dist="t3", k_granularity="channel", group=128),
+    # the c40 shape with group-wise per-token keys and values (32 channels per group)
+    "c40_tgroup": Workload("c40_tgroup", B=1, H=40, d=128, n_q=4680, chunk_len=4680, n_chunks=8,
+                           k_granularity="token_group", group=32),
     "long": Workload("long", B=2, H=48, d=128, n_q=8160, chunk_len=8160, n_chunks=16, masses=True),
 }
 

@@ -28,7 +28,7 @@ def host_u32(t):
 def oracle_formats(w, k_had=True, v_had=True, bits=None, k_signs=(), v_signs=()):
     b = bits or w.bits
     kf = Format(b, w.k_granularity, w.group, k_had, "key", tuple(k_signs))
-    vf = Format(b, "token", w.group, v_had, "value", tuple(v_signs))
+    vf = Format(b, w.v_granularity, w.group, v_had, "value", tuple(v_signs))
     return kf, vf
 
 
@@ -36,7 +36,7 @@ def lib_formats(w, k_had=True, v_had=True, bits=None, k_signs=(), v_signs=()):
     from bit_kv_cache_kvq_amd import kvq
     b = bits or w.bits
     kf = kvq.KvqFormat.make(b, w.k_granularity, w.group, k_had, "key", k_signs or None)
-    vf = kvq.KvqFormat.make(b, "token", w.group, v_had, "value", v_signs or None)
+    vf = kvq.KvqFormat.make(b, w.v_granularity, w.group, v_had, "value", v_signs or None)
     return kf, vf
 
 

@@ -664,3 +664,54 @@ def test_decode_path_variants():
     O, PS, PR = run_gpu(x, w, correction=2)
     Or, PSr, PRr = run_oracle(x, w, correction="exact")
     assert_attention_close(O, Or, "decode exact")
+
+
+# group-wise per-token keys and values (each token's channels in groups of g with their own
+# step and zero point, paper §3): ragged shapes, every row; without the rotation the
+# outlier channels sit in one group, so the groups' steps differ widely
+TGROUP = [
+    dict(B=1, H=2, d=128, n_q=300, chunk_len=100, n_chunks=3, group=32),
+    dict(B=2, H=1, d=128, n_q=70, chunk_len=130, n_chunks=2, group=64),
+    dict(B=1, H=2, d=64, n_q=129, chunk_len=64, n_chunks=3, group=32),
+    dict(B=1, H=1, d=128, n_q=5, chunk_len=1, n_chunks=7, group=32),
+]
+
+
+@pytest.mark.parametrize("shape", TGROUP, ids=lambda s: "x".join(str(v) for v in s.values()))
+@pytest.mark.parametrize("bits,correction,had", [(2, 1, True), (4, 1, True), (2, 0, True), (2, 1, False)])
+def test_token_group_all_rows(shape, bits, correction, had):
+    w = synth.Workload("tgroup", **shape, bits=bits, k_granularity="token_group", seed=11)
+    print(f"attn token_group {shape} bits={bits} c={correction} had={had}", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w, correction=correction, k_had=had, v_had=had)
+    Or, PSr, PRr = run_oracle(x, w, correction=CORR[correction], k_had=had, v_had=had)
+    assert_attention_close(O, Or, f"token_group {shape}")
+    assert_mass_close(PS, PR, PSr, PRr, f"token_group {shape}")
+
+
+def test_token_group_mass_only_and_unsplit():
+    w = synth.Workload("tgroup", B=1, H=3, d=128, n_q=90, chunk_len=200, n_chunks=2, k_granularity="token_group",
+                       group=32, seed=12)
+    print("attn token_group mass-only / unsplit", flush=True)
+    x = synth.draw_all(w)
+    _, PSr, PRr = run_oracle(x, w)
+    _, PS, PR = run_gpu(x, w, mass_only=True)
+    assert_mass_close(PS, PR, PSr, PRr, "token_group mass only")
+    O1, PS1, _ = run_gpu(x, w, split=True)
+    O0, PS0, _ = run_gpu(x, w, split=False)
+    Or, _, _ = run_oracle(x, w)
+    assert_attention_close(O1, Or, "token_group split")
+    assert_attention_close(O0, Or, "token_group unsplit")
+
+
+def test_token_group_c40_sampled_rows():
+    w = synth.WORKLOADS["c40_tgroup"]
+    print("attn c40_tgroup sampled rows", flush=True)
+    x = synth.draw_all(w)
+    O, PS, PR = run_gpu(x, w)
+    rng = np.random.default_rng(5)
+    heads = [(0, 0), (0, 17), (0, 39)]
+    rows = np.sort(rng.choice(w.n_q, 48, replace=False))
+    Or, PSr, PRr = run_oracle(x, w, rows=rows, heads=heads)
+    assert_attention_close(_gather(O, heads, rows), Or, "c40_tgroup")
+    assert_mass_close(_gather(PS, heads, rows), _gather(PR, heads, rows), PSr, PRr, "c40_tgroup")

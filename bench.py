@@ -52,6 +52,15 @@ def traffic_from_profile():
     return float(m_bytes.group(1))
 
 
+def gran_text(w, gran):
+    """Words for a quantization granularity of the workload's keys or values."""
+    if gran == "token_group":
+        return f"per-token groups of {w.group} channels,"
+    if gran == "channel":
+        return f"per-channel ({w.group}-token groups)"
+    return "per-token"
+
+
 def window_memory(w):
     """Device bytes of this workload's cached window (K and V) in INT2, INT4 and bf16: the
     memory a fixed window takes, or the window a fixed budget holds (§1)."""
@@ -110,6 +119,8 @@ def main():
     ap.add_argument("--layers", type=int, default=1,
                     help="independent calls per step (e.g. the layers of one chunk step), run in one batched "
                          "launch (jb_attn_fwd_batch) when above 1")
+    ap.add_argument("--group", type=int, default=0,
+                    help="replace the workload's group size (channels per group for group-wise keys and values)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="only run a device copy of this many MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -140,6 +151,8 @@ def main():
         w = w.replace(bits=args.bits)
     if args.nq:
         w = w.replace(n_q=args.nq)
+    if args.group:
+        w = w.replace(group=args.group)
     t_gen = time.perf_counter()
     x = synth.draw_all(w)
     print(f"# generated {w.name} inputs in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
@@ -235,8 +248,8 @@ def main():
         "dtype": "int8+fp16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} d={w.d}, current chunk {w.n_q} tokens, window "
-                               f"{w.n_chunks}x{w.chunk_len} cached tokens, INT{w.bits} per-{w.k_granularity} K, "
-                               f"per-token V, Hadamard, correction={CORR_NAMES[args.correction]}",
+                               f"{w.n_chunks}x{w.chunk_len} cached tokens, INT{w.bits} {gran_text(w, w.k_granularity)} K, "
+                               f"{gran_text(w, w.v_granularity)} V, Hadamard, correction={CORR_NAMES[args.correction]}",
                    "B": w.B, "H": w.H, "d": w.d, "n_q": w.n_q, "n_c": w.n_c, "bits": w.bits,
                    "parallelism": "none (1 GPU)", "split_workspace_bytes": a.workspace_bytes, "layers": nl,
                    "batched_launch": nl > 1},

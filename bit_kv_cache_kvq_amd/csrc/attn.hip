@@ -69,6 +69,7 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -790,10 +791,11 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         if (tid < D / 4) reinterpret_cast<uint4*>(&ps.dka[0][0])[tid] = gpre;
       }
       if constexpr (TG > 0) {
-        // per-group steps Delta_jg (0 for padding keys), one row per group, M-row order
+        // per-group steps Delta_jg as fp16 bits (0 for padding keys), one row per group,
+        // M-row order, in the per-key table's storage
         if (wave < NG) {
           const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
-          ps.dka[wave][r] = lane < nv ? half_bits_to_f32(pair_bits(gk_d, wave)) : 0.f;
+          reinterpret_cast<uint16_t*>(&ps.dka[0][0])[wave * kBN + r] = lane < nv ? (uint16_t)pair_bits(gk_d, wave) : 0;
         }
       } else if constexpr (!PERCH) {
         const int key = tid & (kBN - 1);
@@ -1065,7 +1067,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     }
     if constexpr (decltype(k_c)::value == kCached && TG > 0) {
       // one exact int32 sum per channel group, scaled by the key's step of that group
-      const float* dkg = &sm.prm[rk_slot].dka[0][0];
+      const _Float16* dkg = reinterpret_cast<const _Float16*>(&sm.prm[rk_slot].dka[0][0]);
       f32x16 sf = {};
 #pragma unroll
       for (int gq = 0; gq < NG; gq++) {
@@ -1079,12 +1081,13 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           a = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[gq * KPG + k2], qlo[gq * KPG + k2], a, 0, 0, 0);
 #pragma unroll
         for (int v4 = 0; v4 < 4; v4++) {
-          const float4 d4 = *reinterpret_cast<const float4*>(&dkg[gq * kBN + 32 * rk_mb + 8 * v4 + 4 * h]);
-          sf[4 * v4 + 0] = fmaf(d4.x, (float)a[4 * v4 + 0], sf[4 * v4 + 0]);
-          sf[4 * v4 + 1] = fmaf(d4.y, (float)a[4 * v4 + 1], sf[4 * v4 + 1]);
-          sf[4 * v4 + 2] = fmaf(d4.z, (float)a[4 * v4 + 2], sf[4 * v4 + 2]);
-          sf[4 * v4 + 3] = fmaf(d4.w, (float)a[4 * v4 + 3], sf[4 * v4 + 3]);
+          const f16x4 d4 = *reinterpret_cast<const f16x4*>(&dkg[gq * kBN + 32 * rk_mb + 8 * v4 + 4 * h]);
+#pragma unroll
+          for (int b = 0; b < 4; b++) sf[4 * v4 + b] = fmaf((float)d4[b], (float)a[4 * v4 + b], sf[4 * v4 + b]);
         }
+        // one group's accumulator at a time: without this fence the groups' MFMA chains
+        // are interleaved and their accumulators spill
+        __builtin_amdgcn_sched_barrier(0);
       }
       sqh[SET] = __builtin_bit_cast(i32x16, sf);
     } else if constexpr (decltype(k_c)::value == kCached) {

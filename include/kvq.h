@@ -5,7 +5,8 @@
  * Compression in Video Diffusion" (Tuncer, Becker, Pfeil; arXiv 2605.26266):
  *   - kvq_pack: the cache compression of §3 -- Hadamard rotation ("Hadamard rotation"),
  *     asymmetric round-to-nearest integer quantization (Eq. (1)) per token or, for keys,
- *     per channel over a group of tokens ("Quantization granularity");
+ *     per channel over a group of tokens, or per group of channels of a token
+ *     ("Quantization granularity");
  *   - jb_attn_fwd: chunk-wise attention of the current chunk's queries over the cached
  *     window and the unquantized current chunk (abstract; §1), with the per-score
  *     correction b subtracted from cached-key scores before the softmax (abstract; Fig. 3
@@ -125,7 +126,8 @@ int kvq_pack(const uint16_t* x, int32_t B, int32_t H, int32_t n, int32_t d, cons
  *   O_i  = (sum_j e^l_ij v_hat_j + sum_r e^l_ir v_r) / sum e^l
  *   P_S,i = sum_j e^l_ij / sum e^l,  P_R,i = sum_r e^l_ir / sum e^l
  * where q' = H q if the keys were rotated (else q), Delta_jc is the key's step size
- * (per token: the same for every c, giving b_ij = s^2 |q_i|^2 Delta_j^2 / 24), and
+ * (per token: the same for every c, giving b_ij = s^2 |q_i|^2 Delta_j^2 / 24; group-wise
+ * per token: the step of c's channel group, giving s^2 sum_groups |q'_i,grp|^2 Delta_j,grp^2 / 24), and
  * b is the second-order Taylor form of the expected inflation of e^l under uniform
  * rounding noise on the cached keys. b_ij = 0 when correction == JB_CORR_NONE.
  * JB_CORR_EXACT replaces b by the logarithm of that inflation itself (Fig. 3 caption's
@@ -147,10 +149,12 @@ typedef struct {
   const uint32_t* k_codes;    /* window layout of k_fmt (role KEY) */
   const uint16_t* k_scale;
   const uint16_t* k_zero;
-  const uint32_t* v_codes;    /* window layout of v_fmt (role VALUE, per token) */
+  const uint32_t* v_codes;    /* window layout of v_fmt (role VALUE) */
   const uint16_t* v_scale;
   const uint16_t* v_zero;
-  kvq_format k_fmt, v_fmt;    /* same bits; k: KEY per token or per channel; v: VALUE per token */
+  kvq_format k_fmt, v_fmt;    /* same bits; k: KEY per token or per channel with v: VALUE per
+                                 token; or both KVQ_PER_TOKEN_GROUP with one group (32 or
+                                 64 < d), correction not JB_CORR_EXACT */
   float softmax_scale;        /* s; 0 selects 1/sqrt(d) */
   int32_t correction;         /* JB_CORR_NONE, JB_CORR_TAYLOR or JB_CORR_EXACT */
   float* o;                   /* fp32 [B, H, n_q, d]: required by fwd, ignored by mass */
@@ -192,7 +196,8 @@ int jb_attn_mass(const jb_attn_args* a, void* stream);
  * call's workspace holds its partials for that count; otherwise
  * no call is split, and each computes exactly what jb_attn_fwd (jb_attn_mass) would for
  * it unsplit. Calls must agree on d, bits, key
- * granularity (and group), and on whether correction is JB_CORR_EXACT; shapes, windows,
+ * granularity (and group; KVQ_PER_TOKEN_GROUP is for single calls only: KVQ_ERR_UNSUPPORTED),
+ * and on whether correction is JB_CORR_EXACT; shapes, windows,
  * rotation flags and signs, softmax scale and the other correction modes may differ.
  * calls points to n_calls host structs, 1 <= n_calls <= KVQ_BATCH_MAX.
  * Errors: the first failing call's jb_attn_fwd (jb_attn_mass) status, KVQ_ERR_NULL

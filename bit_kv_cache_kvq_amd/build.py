@@ -3,6 +3,8 @@
 The quantizer's translation unit is compiled with -ffp-contract=off and correctly
 rounded float32 division, because its codes and fp16 steps must follow one exact
 float32 operation order. All HIP code is compiled without packed-fp32 instructions.
+The host-only unit (argument validation and launch planning) is plain C++ built with
+the host compiler; the translation units compile in parallel.
 """
 from __future__ import annotations
 
@@ -11,6 +13,7 @@ import shutil
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -26,6 +29,8 @@ UNITS = {
     "pack.hip": ["-ffp-contract=off"],
     "attn.hip": [],
 }
+HOST_UNITS = ["host.cpp"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
 
 def hipcc() -> str:
@@ -36,12 +41,16 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP unit and link libkvq.so next to this file; returns its path."""
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="kvq_build_") as tmp:
-        objs = []
+        jobs = []
         for unit, extra in UNITS.items():
             obj = os.path.join(tmp, unit + ".o")
-            cmd = [cc, *COMMON, *extra, "-c", os.path.join(CSRC, unit), "-o", obj]
-            _run(cmd, verbose)
-            objs.append(obj)
+            jobs.append(([cc, *COMMON, *extra, "-c", os.path.join(CSRC, unit), "-o", obj], obj))
+        for unit in HOST_UNITS:
+            obj = os.path.join(tmp, unit + ".o")
+            jobs.append((["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, unit), "-o", obj], obj))
+        with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+            list(ex.map(lambda j: _run(j[0], verbose), jobs))
+        objs = [o for _, o in jobs]
         out = os.path.join(tmp, "libkvq.so")
         _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out], verbose)
         staged = LIB + ".tmp"

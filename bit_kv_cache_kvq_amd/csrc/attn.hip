@@ -80,6 +80,7 @@ constexpr int kStreams = 1;             // 32-query streams per wave
 constexpr int kNS = kWaves * kStreams;  // streams per workgroup
 constexpr int kBM = 32 * kNS;           // queries per workgroup
 constexpr int kBN = 64;                 // keys per tile
+static_assert(kBM == kQueryBlock && kBN == kKeyTile, "the host plan and the kernels use one geometry");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPmax = 32768.f;     // largest fp16 row sum of a block accepted in a pass
 constexpr float kHeadroom = 2.f;     // first reference max: the first block's max + 2 (log2 units)
@@ -2015,62 +2016,6 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
   if (h == 0) *reinterpret_cast<float4*>(rec + D) = make_float4(m_run, ls, 0.f, 0.f);
 }
 
-int validate_attn(const jb_attn_args* a, bool mass_only) {
-  if (!a) return KVQ_ERR_NULL;
-  const kvq_format& kf = a->k_fmt;
-  const kvq_format& vf = a->v_fmt;
-  if (kf.bits != 2 && kf.bits != 4) return KVQ_ERR_UNSUPPORTED;
-  if (vf.bits != kf.bits) return KVQ_ERR_UNSUPPORTED;
-  if (kf.role != KVQ_ROLE_KEY || vf.role != KVQ_ROLE_VALUE) return KVQ_ERR_UNSUPPORTED;
-  if (kf.granularity == KVQ_PER_TOKEN_GROUP || vf.granularity == KVQ_PER_TOKEN_GROUP) {
-    // group-wise keys and values together, one group size, second-order correction
-    if (kf.granularity != vf.granularity || kf.group != vf.group) return KVQ_ERR_UNSUPPORTED;
-    if ((kf.group != 32 && kf.group != 64) || kf.group >= a->d) return KVQ_ERR_UNSUPPORTED;
-    if (a->correction == JB_CORR_EXACT) return KVQ_ERR_UNSUPPORTED;
-  } else {
-    if (vf.granularity != KVQ_PER_TOKEN) return KVQ_ERR_UNSUPPORTED;
-    if (kf.granularity != KVQ_PER_TOKEN && kf.granularity != KVQ_PER_CHANNEL) return KVQ_ERR_UNSUPPORTED;
-  }
-  if (kf.granularity == KVQ_PER_CHANNEL && kf.group != 64 && kf.group != 128) return KVQ_ERR_UNSUPPORTED;
-  if ((kf.hadamard | vf.hadamard) & ~1) return KVQ_ERR_UNSUPPORTED;
-  for (const kvq_format* f : {&kf, &vf}) {
-    const uint32_t any = f->signs[0] | f->signs[1] | f->signs[2] | f->signs[3];
-    if (any && !f->hadamard) return KVQ_ERR_UNSUPPORTED;
-    if (a->d == 64 && (f->signs[2] | f->signs[3])) return KVQ_ERR_UNSUPPORTED;
-  }
-  if (a->correction != JB_CORR_NONE && a->correction != JB_CORR_TAYLOR && a->correction != JB_CORR_EXACT)
-    return KVQ_ERR_UNSUPPORTED;
-  if (a->d != 64 && a->d != 128) return KVQ_ERR_SHAPE;
-  if (a->B < 1 || a->H < 1 || a->n_q < 1 || a->n_r < 0 || a->chunk_len < 1 || a->n_chunks < 0)
-    return KVQ_ERR_SHAPE;
-  if ((long long)a->n_chunks * a->chunk_len + a->n_r < 1) return KVQ_ERR_SHAPE;
-  if (a->window_chunks < 0 || (a->window_chunks > 0 && a->window_chunks < a->n_chunks)) return KVQ_ERR_SHAPE;
-  if (!(a->softmax_scale >= 0.f) || isinf(a->softmax_scale)) return KVQ_ERR_SHAPE;
-  // the kernel addresses one head's cached codes through 32-bit buffer offsets
-  if ((long long)a->n_chunks * chunk_pad(a->chunk_len) * a->d * kf.bits / 8 > 0x7FFFFFFFLL) return KVQ_ERR_SHAPE;
-  const long long nqblk = (a->n_q + kBM - 1) / kBM;
-  if (nqblk * a->B * a->H > 0x7FFFFFFFLL) return KVQ_ERR_SHAPE;
-  if (!a->q) return KVQ_ERR_NULL;
-  if (a->n_r > 0 && (!a->k_cur || (!mass_only && !a->v_cur))) return KVQ_ERR_NULL;
-  if (a->n_chunks > 0) {
-    if (!a->k_codes || !a->k_scale || !a->k_zero) return KVQ_ERR_NULL;
-    if (!mass_only && (!a->v_codes || !a->v_scale || !a->v_zero)) return KVQ_ERR_NULL;
-    if (!aligned16(a->k_codes) || !aligned16(a->k_scale) || !aligned16(a->k_zero)) return KVQ_ERR_ALIGN;
-    if (!mass_only && (!aligned16(a->v_codes) || !aligned16(a->v_scale) || !aligned16(a->v_zero)))
-      return KVQ_ERR_ALIGN;
-  }
-  if (mass_only) {
-    if (!a->mass_s || !a->mass_r) return KVQ_ERR_NULL;
-  } else {
-    if (!a->o) return KVQ_ERR_NULL;
-    if (!a->mass_s != !a->mass_r) return KVQ_ERR_NULL;
-    if (!aligned16(a->o)) return KVQ_ERR_ALIGN;
-  }
-  if (!aligned16(a->q)) return KVQ_ERR_ALIGN;
-  if (a->n_r > 0 && (!aligned16(a->k_cur) || (!mass_only && !aligned16(a->v_cur)))) return KVQ_ERR_ALIGN;
-  return KVQ_OK;
-}
-
 // Combines the partial records of the n_split shares of each query: with M the largest
 // reference max, weights w = 2^(m - M); O = sum w acc / sum w (l_S + l_R), and the
 // masses from the weighted sums. One thread per (query, 4 output channels); G threads
@@ -2180,73 +2125,20 @@ __global__ __launch_bounds__(256) void jb_merge_records_kernel(const float* __re
   }
 }
 
-struct AttnPlan {
-  int n_qblk, n_split;
-  size_t part_bytes;  // workspace the split needs (0 for n_split == 1)
-  int dec_shares;     // few queries: shares of the cached tiles per head (0: no decode path)
-  size_t dec_bytes;   // workspace of the decode path's partial records
-};
-
-// Splits each query block's tile sequence over n_split workgroups when that shortens the
-// critical path: with C compute units and one workgroup per unit at a time, a grid of g
-// workgroups over T tiles takes about ceil(g S / C) rounds of ceil(T / S) tiles. A split
-// is taken only for a gain of at least 10% (the partials cost a combine pass).
-// Shares per query block for a launch of `grid` query-block workgroups over `tiles` tiles
-// each, on `cus` compute units: the cost is the rounds of the device times the tiles of
-// the longest share; a split (partial records, a merge, a prologue per share) is taken
-// only for a predicted gain of a quarter or more.
-int choose_split(long long grid, long long tiles, int cus) {
-  auto cost = [&](long long S) { return ((grid * S + cus - 1) / cus) * ((tiles + S - 1) / S); };
-  long long best = cost(1);
-  int n_split = 1;
-  for (int S = 2; S <= 8 && S <= tiles; S++) {
-    if (grid * S > 0x7FFFFFFFLL) break;
-    const long long c = cost(S);
-    if (4 * c <= 3 * best) {
-      best = c;
-      n_split = S;
-    }
-  }
-  return n_split;
-}
-
-AttnPlan plan_attn(const jb_attn_args* a) {
-  AttnPlan pl;
-  pl.n_qblk = (a->n_q + kBM - 1) / kBM;
-  pl.n_split = 1;
-  pl.part_bytes = 0;
-  pl.dec_shares = 0;
-  pl.dec_bytes = 0;
+// Compute units of the current device (0 if it cannot be queried: no split, no decode path).
+int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 1) {
     (void)hipGetLastError();
-    return pl;
+    return 0;
   }
-  // At most 32 queries (one stream) with per-token keys and a cached window: the decode
-  // path, with as many one-wave shares (the window's, plus one per head for its current
-  // chunk) as fit on the device at once (two per SIMD)
-  const long long n_ct = (long long)a->n_chunks * (chunk_pad(a->chunk_len) / kBN);
-  if (a->n_q <= 32 && a->k_fmt.granularity == KVQ_PER_TOKEN && a->correction != JB_CORR_EXACT && n_ct > 0) {
-    const long long bhc = (long long)a->B * a->H;
-    const long long S = std::min(n_ct, std::max(1LL, 8LL * cus / bhc - (a->n_r > 0 ? 1 : 0)));
-    if ((S + 1) * bhc <= 0x7FFFFFFFLL) {
-      pl.dec_shares = (int)S;
-      pl.dec_bytes = (size_t)(S + (a->n_r > 0 ? 1 : 0)) * bhc * a->n_q * (size_t)(a->d + 4) * sizeof(float);
-    }
-  }
-  const long long grid = (long long)pl.n_qblk * a->B * a->H;
-  const long long tiles = (long long)a->n_chunks * (chunk_pad(a->chunk_len) / kBN) + (a->n_r + kBN - 1) / kBN;
-  pl.n_split = choose_split(grid, tiles, cus);
-  if (pl.n_split > 1)
-    pl.part_bytes = (size_t)pl.n_split * a->B * a->H * a->n_q * (size_t)(a->d + 4) * sizeof(float);
-  return pl;
+  return cus;
 }
 
-// Kernel parameters of one call under plan pl; launches the query rotation pre-pass when
-// the plan has room for it in the workspace.
+// Kernel parameters of one call under plan pl (split partials in the call's workspace).
 template <int D, bool MASS_ONLY, bool PERCH>
-Params fill_params(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
+Params fill_params(const jb_attn_args* a, const AttnPlan& pl) {
   Params p;
   p.B = a->B;
   p.H = a->H;
@@ -2286,7 +2178,7 @@ Params fill_params(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
 
 template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT = false, int TG = 0>
 int launch_attn(const jb_attn_args* a, const AttnPlan& pl, hipStream_t st) {
-  const Params p = fill_params<D, MASS_ONLY, PERCH>(a, pl, st);
+  const Params p = fill_params<D, MASS_ONLY, PERCH>(a, pl);
   const unsigned grid = (unsigned)(pl.n_qblk * a->B * a->H * pl.n_split);
   jb_attn_kernel<D, BITS, MASS_ONLY, PERCH, EXACT, TG><<<grid, kThreads, 0, st>>>(p);
   if (pl.n_split > 1) {
@@ -2305,7 +2197,7 @@ int launch_decode(const jb_attn_args* a, const AttnPlan& pl0, hipStream_t st) {
   AttnPlan pl = pl0;
   pl.n_split = 1;
   pl.part_bytes = 0;
-  Params p = fill_params<D, MASS_ONLY, false>(a, pl, st);
+  Params p = fill_params<D, MASS_ONLY, false>(a, pl);
   const int S = pl.dec_shares;
   const size_t rows = (size_t)a->B * a->H * a->n_q;
   float* part = static_cast<float*>(a->workspace);
@@ -2316,25 +2208,29 @@ int launch_decode(const jb_attn_args* a, const AttnPlan& pl0, hipStream_t st) {
   return launch_status();
 }
 
+// A call with a workspace runs the plan (decode path, or split when the grid is small for
+// the device); one without runs the main kernel unsplit. A workspace smaller than the plan
+// needs is an error.
 template <bool MASS_ONLY>
 int dispatch(const jb_attn_args* a, void* stream) {
   const int st = validate_attn(a, MASS_ONLY);
   if (st) return st;
-  AttnPlan pl = plan_attn(a);
-  const size_t have = a->workspace ? a->workspace_bytes : 0;
-  if (pl.dec_shares && have >= pl.dec_bytes) {
-    if (!aligned16(a->workspace)) return KVQ_ERR_ALIGN;
+  AttnPlan pl = plan_attn(a, device_cus());
+  const size_t need = plan_workspace(pl);
+  if (a->workspace) {
+    if (a->workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (need && !aligned16(a->workspace)) return KVQ_ERR_ALIGN;
+  } else {
+    pl.dec_shares = 0;
+    pl.n_split = 1;
+    pl.part_bytes = 0;
+  }
+  if (pl.dec_shares) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (a->d == 128)
       return a->k_fmt.bits == 2 ? launch_decode<128, 2, MASS_ONLY>(a, pl, s) : launch_decode<128, 4, MASS_ONLY>(a, pl, s);
     return a->k_fmt.bits == 2 ? launch_decode<64, 2, MASS_ONLY>(a, pl, s) : launch_decode<64, 4, MASS_ONLY>(a, pl, s);
   }
-  // the workspace holds the split partials; without room the grid runs unsplit
-  if (pl.n_split > 1 && have < pl.part_bytes) {
-    pl.n_split = 1;
-    pl.part_bytes = 0;
-  }
-  if (pl.n_split > 1 && !aligned16(a->workspace)) return KVQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool perch = a->k_fmt.granularity == KVQ_PER_CHANNEL;
   if (a->k_fmt.granularity == KVQ_PER_TOKEN_GROUP) {
@@ -2375,34 +2271,17 @@ int launch_batch(const jb_attn_args* calls, int n, hipStream_t st) {
   // One split count S for the whole batch, chosen as for a single call but over the
   // workgroups of all calls: rounds of the device times the longest share. It is used
   // only when every call's workspace holds its S partials.
+  const int S = batch_split(calls, n, device_cus());
   AttnPlan pl[kMaxBatch];
-  long long grid1 = 0, tiles = 0;
-  for (int c = 0; c < n; c++) {
-    const jb_attn_args* a = &calls[c];
-    pl[c] = plan_attn(a);
-    grid1 += (long long)pl[c].n_qblk * a->B * a->H;
-    tiles = std::max(tiles, (long long)a->n_chunks * (chunk_pad(a->chunk_len) / kBN) + (a->n_r + kBN - 1) / kBN);
-  }
-  int S = 1;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
-                                               hipSuccess && cus > 0)
-    S = choose_split(grid1, tiles, cus);
-  else
-    (void)hipGetLastError();
-  for (int c = 0; c < n && S > 1; c++) {
-    const jb_attn_args* a = &calls[c];
-    const size_t part = (size_t)S * a->B * a->H * a->n_q * (size_t)(a->d + 4) * sizeof(float);
-    if (!a->workspace || !aligned16(a->workspace) || a->workspace_bytes < part) S = 1;
-  }
   BatchParams bp;
   bp.n = n;
   long long next = 0;
   for (int c = 0; c < n; c++) {
     const jb_attn_args* a = &calls[c];
+    pl[c] = plan_attn(a, 0);
     pl[c].n_split = S;
-    pl[c].part_bytes = S > 1 ? (size_t)S * a->B * a->H * a->n_q * (size_t)(a->d + 4) * sizeof(float) : 0;
-    bp.p[c] = fill_params<D, MASS_ONLY, PERCH>(a, pl[c], st);
+    pl[c].part_bytes = S > 1 ? partial_bytes(a, S) : 0;
+    bp.p[c] = fill_params<D, MASS_ONLY, PERCH>(a, pl[c]);
     bp.grid[c] = (int)(pl[c].n_qblk * a->B * a->H * S);
     bp.start[c] = (int)next;
     next += ((long long)bp.grid[c] + 7) / 8 * 8;
@@ -2422,23 +2301,9 @@ int launch_batch(const jb_attn_args* calls, int n, hipStream_t st) {
 
 template <bool MASS_ONLY>
 int dispatch_batch(const jb_attn_args* calls, int n, void* stream) {
-  if (!calls) return KVQ_ERR_NULL;
-  if (n < 1 || n > kMaxBatch) return KVQ_ERR_SHAPE;
+  const int st = validate_batch(calls, n, MASS_ONLY);
+  if (st) return st;
   const jb_attn_args& a0 = calls[0];
-  for (int c = 0; c < n; c++) {
-    const int st = validate_attn(&calls[c], MASS_ONLY);
-    if (st) return st;
-    const jb_attn_args& a = calls[c];
-    if (a.k_fmt.granularity == KVQ_PER_TOKEN_GROUP) return KVQ_ERR_UNSUPPORTED;  // single calls only
-    if (a.d != a0.d || a.k_fmt.bits != a0.k_fmt.bits || a.k_fmt.granularity != a0.k_fmt.granularity ||
-        (a.k_fmt.granularity == KVQ_PER_CHANNEL && a.k_fmt.group != a0.k_fmt.group) ||
-        (a.correction == JB_CORR_EXACT) != (a0.correction == JB_CORR_EXACT))
-      return KVQ_ERR_UNSUPPORTED;
-  }
-  long long total = 0;
-  for (int c = 0; c < n; c++)
-    total += ((long long)(calls[c].n_q + kBM - 1) / kBM * calls[c].B * calls[c].H * 8 + 7) / 8 * 8;
-  if (total > 0x7FFFFFFFLL) return KVQ_ERR_SHAPE;  // room for up to 8 shares per call
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool perch = a0.k_fmt.granularity == KVQ_PER_CHANNEL;
   const bool exact = a0.correction == JB_CORR_EXACT;
@@ -2474,7 +2339,6 @@ extern "C" int jb_attn_fwd(const jb_attn_args* a, void* stream) { return kvq::di
 extern "C" int jb_attn_mass(const jb_attn_args* a, void* stream) { return kvq::dispatch<true>(a, stream); }
 
 extern "C" size_t jb_attn_workspace_bytes(const jb_attn_args* a) {
-  if (kvq::validate_attn(a, false) != KVQ_OK && kvq::validate_attn(a, true) != KVQ_OK) return 0;
-  const kvq::AttnPlan pl = kvq::plan_attn(a);
-  return pl.dec_shares ? pl.dec_bytes : pl.part_bytes;
+  if (kvq::validate_attn(a, false) != KVQ_OK && kvq::validate_attn(a, true) != KVQ_OK) return SIZE_MAX;
+  return kvq::plan_workspace(kvq::plan_attn(a, kvq::device_cus()));
 }

@@ -242,20 +242,6 @@ __global__ __launch_bounds__(GROUP * D / 16) void pack_channel_kernel(
   }
 }
 
-int validate_format(const kvq_format* f) {
-  if (!f) return KVQ_ERR_NULL;
-  if (f->bits != 2 && f->bits != 4) return KVQ_ERR_UNSUPPORTED;
-  if (f->hadamard != 0 && f->hadamard != 1) return KVQ_ERR_UNSUPPORTED;
-  if (!f->hadamard && (f->signs[0] | f->signs[1] | f->signs[2] | f->signs[3])) return KVQ_ERR_UNSUPPORTED;
-  if (f->role != KVQ_ROLE_KEY && f->role != KVQ_ROLE_VALUE) return KVQ_ERR_UNSUPPORTED;
-  if (f->granularity == KVQ_PER_TOKEN) return KVQ_OK;
-  if (f->granularity == KVQ_PER_TOKEN_GROUP) return f->group == 32 || f->group == 64 ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
-  if (f->granularity != KVQ_PER_CHANNEL) return KVQ_ERR_UNSUPPORTED;
-  if (f->role != KVQ_ROLE_KEY) return KVQ_ERR_UNSUPPORTED;
-  if (f->group != 64 && f->group != 128) return KVQ_ERR_UNSUPPORTED;
-  return KVQ_OK;
-}
-
 template <int D, int BITS>
 int launch_pack(const uint16_t* x, int B, int H, int n, const kvq_format* f, int n_chunks, int chunk_idx,
                 uint32_t* codes, uint16_t* scale, uint16_t* zero, hipStream_t st) {
@@ -305,55 +291,15 @@ int launch_pack(const uint16_t* x, int B, int H, int n, const kvq_format* f, int
 
 using namespace kvq;
 
-extern "C" int32_t kvq_chunk_pad(int32_t chunk_len) { return chunk_len < 1 ? 0 : kvq::chunk_pad(chunk_len); }
-
-extern "C" int kvq_window_elems(const kvq_format* fmt, int32_t B, int32_t H, int32_t d, int32_t chunk_len,
-                                int32_t n_chunks, size_t* code_words, size_t* param_elems) {
-  int st = validate_format(fmt);
-  if (st) return st;
-  if (!code_words || !param_elems) return KVQ_ERR_NULL;
-  if (B < 1 || H < 1 || chunk_len < 1 || n_chunks < 0 || (d != 64 && d != 128)) return KVQ_ERR_SHAPE;
-  const size_t cp = (size_t)kvq::chunk_pad(chunk_len);
-  const size_t bh = (size_t)B * H;
-  *code_words = bh * n_chunks * cp * d * fmt->bits / 32;
-  if (fmt->granularity == KVQ_PER_TOKEN)
-    *param_elems = bh * n_chunks * cp;
-  else if (fmt->granularity == KVQ_PER_TOKEN_GROUP)
-    *param_elems = bh * n_chunks * cp * (size_t)(fmt->group < d ? d / fmt->group : 1);
-  else
-    *param_elems = bh * n_chunks * (size_t)((chunk_len + fmt->group - 1) / fmt->group) * d;
-  return KVQ_OK;
-}
-
 extern "C" int kvq_pack(const uint16_t* x, int32_t B, int32_t H, int32_t n, int32_t d, const kvq_format* fmt,
                         int32_t n_chunks, int32_t chunk_idx, uint32_t* codes, uint16_t* scale, uint16_t* zero,
                         void* stream) {
-  int st = validate_format(fmt);
+  const int st = validate_pack(x, B, H, n, d, fmt, n_chunks, chunk_idx, codes, scale, zero);
   if (st) return st;
-  if (!x || !codes || !scale || !zero) return KVQ_ERR_NULL;
-  if (B < 1 || H < 1 || n < 1 || n_chunks < 1 || chunk_idx < 0 || chunk_idx >= n_chunks) return KVQ_ERR_SHAPE;
-  if (d != 64 && d != 128) return KVQ_ERR_SHAPE;
-  if (d == 64 && (fmt->signs[2] | fmt->signs[3])) return KVQ_ERR_UNSUPPORTED;
-  if (fmt->granularity == KVQ_PER_TOKEN_GROUP && fmt->group >= d) return KVQ_ERR_UNSUPPORTED;
-  if ((long long)B * H > 65535) return KVQ_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scale) || !aligned16(zero)) return KVQ_ERR_ALIGN;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d == 128)
     return fmt->bits == 2 ? launch_pack<128, 2>(x, B, H, n, fmt, n_chunks, chunk_idx, codes, scale, zero, s)
                           : launch_pack<128, 4>(x, B, H, n, fmt, n_chunks, chunk_idx, codes, scale, zero, s);
   return fmt->bits == 2 ? launch_pack<64, 2>(x, B, H, n, fmt, n_chunks, chunk_idx, codes, scale, zero, s)
                         : launch_pack<64, 4>(x, B, H, n, fmt, n_chunks, chunk_idx, codes, scale, zero, s);
-}
-
-extern "C" const char* kvq_status_str(int status) {
-  switch (status) {
-    case KVQ_OK: return "ok";
-    case KVQ_ERR_NULL: return "a required pointer is NULL";
-    case KVQ_ERR_SHAPE: return "a size is out of range or inconsistent";
-    case KVQ_ERR_UNSUPPORTED: return "unsupported format or option combination";
-    case KVQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
-    case KVQ_ERR_HIP: return "HIP launch failed";
-    default: return "unknown status";
-  }
 }

@@ -216,8 +216,15 @@ def jb_attn_mass_batch(calls, stream=None):
     _batch("jb_attn_mass_batch", calls, stream)
 
 
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+
 def jb_attn_workspace_bytes(args: JbAttnArgs) -> int:
-    return int(_lib.jb_attn_workspace_bytes(ctypes.byref(args)))
+    """Workspace bytes the call uses on the current device (0: none); raises on invalid arguments."""
+    n = int(_lib.jb_attn_workspace_bytes(ctypes.byref(args)))
+    if n == SIZE_MAX:
+        raise ValueError("jb_attn_workspace_bytes: invalid attention arguments (jb_attn_fwd would refuse them)")
+    return n
 
 
 def attach_workspace(args: JbAttnArgs, device="cuda"):

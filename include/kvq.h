@@ -43,7 +43,7 @@ enum {
   KVQ_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
   KVQ_ERR_UNSUPPORTED = -3, /* a format/option combination this library does not implement */
   KVQ_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
-  KVQ_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  KVQ_ERR_WORKSPACE = -5,   /* a workspace smaller than the call needs (jb_attn_workspace_bytes) */
   KVQ_ERR_HIP = -6          /* the HIP launch failed */
 };
 
@@ -182,7 +182,8 @@ typedef struct {
  * Errors: KVQ_ERR_NULL, KVQ_ERR_SHAPE (also when one head's cached codes exceed 2^31 - 1
  * bytes), KVQ_ERR_UNSUPPORTED (mixed bits, value per-channel, wrong roles, group not
  * 64/128, signs without hadamard or past channel d), KVQ_ERR_ALIGN (also a misaligned
- * workspace that a split would use), KVQ_ERR_HIP. */
+ * workspace that a split would use), KVQ_ERR_WORKSPACE (a workspace was given but is
+ * smaller than jb_attn_workspace_bytes reports), KVQ_ERR_HIP. */
 int jb_attn_fwd(const jb_attn_args* a, void* stream);
 
 /* Attention masses only (Fig. 2): writes mass_s and mass_r; o and values are not read. */
@@ -211,7 +212,7 @@ int jb_attn_mass_batch(const jb_attn_args* calls, int32_t n_calls, void* stream)
  * the size jb_attn_workspace_bytes reports, the call streams each head's cached window in
  * one-wave shares (a decode-like regime, bound by the cache stream rather than the matrix
  * cores), computes the current chunk as one more share and merges the shares' partial
- * records; without it, the main kernel runs unsplit. */
+ * records; without a workspace (NULL), the main kernel runs unsplit. */
 
 /* Workspace bytes a call with these arguments uses on the current device (0: none).
  * When the grid of query blocks is small for the device (fewer workgroups than its compute
@@ -219,10 +220,12 @@ int jb_attn_mass_batch(const jb_attn_args* calls, int32_t n_calls, void* stream)
  * window, then current chunk) into up to 8 contiguous shares, one workgroup each, writes
  * one partial record per share and query (unnormalized sum, reference max, l_S, l_R:
  * fp32 [shares][B*H][n_q][d + 4]) into the workspace and combines them in a second kernel
- * on the same stream. A call given no workspace, or one smaller than this size, runs
- * unsplit; the two differ by rounding only (each share takes its fp16 numerators
- * relative to its own reference max). The workspace must not be shared by calls that may
- * run concurrently. Returns 0 for invalid arguments. */
+ * on the same stream. A call given no workspace (NULL) runs unsplit on the main kernel;
+ * the two differ by rounding only (each share takes its fp16 numerators relative to its
+ * own reference max). A call given a workspace smaller than this size fails with
+ * KVQ_ERR_WORKSPACE before anything is launched. The workspace must not be shared by calls
+ * that may run concurrently. Returns 0 when the call needs no workspace on this device and
+ * SIZE_MAX when the arguments are invalid (jb_attn_fwd would return a negative status). */
 size_t jb_attn_workspace_bytes(const jb_attn_args* a);
 
 /* Static description of a status code. */

@@ -58,6 +58,11 @@ def test_geometry(kvq):
     assert kvq.window_shapes(f, 1, 40, 128, 4680, 8) == ((1, 40, 37888, 16), (1, 40, 296, 128))
     f = kvq.KvqFormat.make(2, "token_group", 32, True, "value")
     assert kvq.window_shapes(f, 1, 40, 128, 4680, 8) == ((1, 40, 592, 128, 4), (1, 40, 37888, 4))
+    # a channel group must be narrower than d (a group of d channels is the per-token format)
+    cw, pe = ctypes.c_size_t(), ctypes.c_size_t()
+    f64 = kvq.KvqFormat.make(2, "token_group", 64, True, "key")
+    assert kvq._lib.kvq_window_elems(ctypes.byref(f64), 1, 1, 64, 128, 1, ctypes.byref(cw), ctypes.byref(pe)) == -3
+    assert kvq._lib.kvq_window_elems(ctypes.byref(f64), 1, 1, 128, 128, 1, ctypes.byref(cw), ctypes.byref(pe)) == 0
     f = kvq.KvqFormat.make(4, "token_group", 64, True, "key")
     assert kvq.window_shapes(f, 2, 3, 128, 100, 2) == ((2, 3, 256, 16), (2, 3, 256, 2))
     # bytes per token and head at d=128: INT2 32 + 4, INT4 64 + 4 (codes + fp16 step and zero)
@@ -136,6 +141,12 @@ def test_attn_validation_without_launch(kvq):
     assert fwd(args(softmax_scale=-1.0)) == -2
     assert mass(args()) == -1                   # mass needs mass_s / mass_r
     assert lib.jb_attn_workspace_bytes(ctypes.byref(args())) == 0   # no device here: no split planned
+    size_max = ctypes.c_size_t(-1).value
+    assert lib.jb_attn_workspace_bytes(ctypes.byref(args(softmax_scale=-1.0))) == size_max  # invalid arguments
+    assert lib.jb_attn_workspace_bytes(None) == size_max
+    with pytest.raises(ValueError):
+        kvq.jb_attn_workspace_bytes(args(q=P + 2, o=None, mass_s=None))
+    assert kvq.kvq_status_str(-5).startswith("workspace smaller")
 
 
 def test_batch_validation_without_launch(kvq):

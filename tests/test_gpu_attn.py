@@ -108,6 +108,16 @@ def test_workload_sampled_rows(name, nrows):
     assert_attention_close(_gather(O, heads, rows), Or, name)
     assert_mass_close(_gather(PS, heads, rows), _gather(PR, heads, rows), PSr, PRr, name)
     assert np.all(np.isfinite(O))
+    if name == "long":
+        # every row of one head of the long window, from the same call (its peakiest rows
+        # carry the largest errors; regenerating the 8 GB of inputs for a test of its own
+        # would double the cost)
+        head = (1, 40)
+        print(f"attn long: every row of head {head}", flush=True)
+        Or, PSr, PRr = run_oracle(x, w, heads=[head])
+        b, h = head
+        assert_attention_close(O[b, h][None, None], Or, f"long head {head}")
+        assert_mass_close(PS[b, h][None, None], PR[b, h][None, None], PSr, PRr, f"long head {head}")
 
 
 # every row of a few full-size heads (head (0, 12) of c40 holds rows whose attention mass
@@ -133,10 +143,16 @@ def test_c40_int4_sampled_rows():
     x = synth.draw_all(w)
     O, PS, PR = run_gpu(x, w)
     rows = np.arange(0, w.n_q, 97)
-    heads = [(0, 5)]
+    heads = [(0, 5), (0, 33)]
     Or, PSr, PRr = run_oracle(x, w, rows=rows, heads=heads)
     assert_attention_close(_gather(O, heads, rows), Or, "c40 int4")
     assert_mass_close(_gather(PS, heads, rows), _gather(PR, heads, rows), PSr, PRr, "c40 int4")
+    # every row of one head
+    head = (0, 12)
+    print(f"attn c40 int4: every row of head {head}", flush=True)
+    Or, PSr, PRr = run_oracle(x, w, heads=[head])
+    assert_attention_close(O[0, 12][None, None], Or, f"c40 int4 head {head}")
+    assert_mass_close(PS[0, 12][None, None], PR[0, 12][None, None], PSr, PRr, f"c40 int4 head {head}")
 
 
 # ragged and degenerate shapes, every row checked
@@ -186,7 +202,7 @@ def test_per_channel_keys_all_rows(shape, bits, correction):
 @pytest.mark.parametrize("shape", PERCH[:2], ids=lambda s: "x".join(str(v) for v in s.values()))
 def test_per_channel_keys_without_workspace(shape):
     """Per-channel keys with and without a workspace (with one the call may split; a
-    workspace too small for the split partials runs unsplit)."""
+    workspace too small for the split partials is refused before any launch)."""
     w = synth.Workload("perch", **shape, bits=2, k_dist="t3", k_granularity="channel", seed=11)
     print(f"attn per-channel {shape} without workspace", flush=True)
     x = synth.draw_all(w)
@@ -194,11 +210,14 @@ def test_per_channel_keys_without_workspace(shape):
     assert run_gpu.last_workspace_bytes == 0
     b = run_gpu(x, w, split=True)
     assert run_gpu.last_workspace_bytes > 0
-    # a workspace one record short of the split: the call runs unsplit
+    # a workspace one record short of the split: KVQ_ERR_WORKSPACE, outputs untouched
     assert run_gpu.wanted_workspace_bytes > 16, "expected a split plan"
-    c = run_gpu(x, w, ws_bytes=run_gpu.wanted_workspace_bytes - 16)
+    kvq = _kvq()
+    with pytest.raises(kvq.KvqError) as err:
+        run_gpu(x, w, ws_bytes=run_gpu.wanted_workspace_bytes - 16)
+    assert err.value.status == -5
     Or, PSr, PRr = run_oracle(x, w)
-    for label, r in (("no workspace", a), ("workspace", b), ("short workspace", c)):
+    for label, r in (("no workspace", a), ("workspace", b)):
         assert_attention_close(r[0], Or, f"perch {label}")
         assert_mass_close(r[1], r[2], PSr, PRr, f"perch {label}")
 
@@ -425,8 +444,8 @@ def test_mass_ablation_against_bf16(name):
 
 
 # Randomized rotation H diag(s) (keys and queries) and H diag(t) (values), every row:
-# per-token and per-channel keys, both widths, with and without a workspace (per-channel
-# keys rotate the queries in a pre-pass when there is one), and sampled rows of c40.
+# per-token and per-channel keys, both widths, with and without a workspace (with one,
+# the call may run split over the window), and sampled rows of c40.
 SIGN_SHAPES = [
     dict(B=1, H=2, d=128, n_q=200, chunk_len=150, n_chunks=3),
     dict(B=2, H=1, d=64, n_q=90, chunk_len=70, n_chunks=2),
@@ -559,6 +578,56 @@ def test_batched_calls(gran):
             O1, PS1, PR1 = run_gpu(x, w, correction=opt["correction"], scale=opt.get("scale", 0.0), split=False, **sg)
             np.testing.assert_array_equal(O, O1)
             np.testing.assert_array_equal(PS, PS1)
+
+
+@pytest.mark.parametrize("gran", ["token", "channel"])
+@pytest.mark.parametrize("split", [False, True])
+def test_batched_calls_exact_correction(gran, split):
+    """jb_attn_fwd_batch with JB_CORR_EXACT on every call (the exact kernels), unsplit and,
+    with workspaces, split over the batch, against the oracle's exact correction."""
+    kvq = _kvq()
+    calls, outs, keep, specs, wss = [], [], [], [], []
+    for i, (shape, opt) in enumerate(BATCH_SHAPES):
+        w = synth.Workload("batchx", **shape, k_granularity=gran, group=64,
+                           k_dist="t3" if gran == "channel" else "outlier", seed=60 + i)
+        x = synth.draw_all(w)
+        a, out, kp = _prepare(x, w, correction=2, scale=opt.get("scale", 0.0))
+        if split:
+            wss.append(kvq.attach_workspace(a))
+        calls.append(a)
+        outs.append(out)
+        keep.append(kp)
+        specs.append((w, x, opt))
+    print(f"attn batch exact {gran} split={split}: {len(calls)} calls", flush=True)
+    kvq.jb_attn_fwd_batch(calls)
+    torch.cuda.synchronize()
+    for (w, x, opt), (o, ms, mr) in zip(specs, outs):
+        Or, PSr, PRr = run_oracle(x, w, correction="exact", scale=opt.get("scale") or None)
+        assert_attention_close(o.cpu().numpy(), Or, f"batch exact {gran} {w.B}x{w.H}x{w.n_q}")
+        assert_mass_close(ms.cpu().numpy(), mr.cpu().numpy(), PSr, PRr, f"batch exact {gran} {w.B}x{w.H}x{w.n_q}")
+
+
+def test_batched_mass_only_per_channel():
+    """jb_attn_mass_batch with per-channel keys (groups of 64 and, in a second batch, 128),
+    Taylor and no correction, against the oracle's masses."""
+    kvq = _kvq()
+    for group in (64, 128):
+        calls, outs, keep, specs = [], [], [], []
+        for i, (shape, opt) in enumerate(BATCH_SHAPES):
+            w = synth.Workload("batchmc", **shape, k_granularity="channel", group=group, k_dist="t3", seed=70 + i)
+            x = synth.draw_all(w)
+            a, out, kp = _prepare(x, w, correction=opt["correction"], scale=opt.get("scale", 0.0))
+            calls.append(a)
+            outs.append(out)
+            keep.append(kp)
+            specs.append((w, x, opt))
+        print(f"attn batch: masses only, per-channel keys in groups of {group}", flush=True)
+        kvq.jb_attn_mass_batch(calls)
+        torch.cuda.synchronize()
+        for (w, x, opt), (o, ms, mr) in zip(specs, outs):
+            _, PSr, PRr = run_oracle(x, w, correction=CORR[opt["correction"]], scale=opt.get("scale") or None)
+            assert_mass_close(ms.cpu().numpy(), mr.cpu().numpy(), PSr, PRr,
+                              f"batch mass perch g{group} {w.B}x{w.H}x{w.n_q}")
 
 
 def test_batched_calls_with_workspaces_split_together():

@@ -56,6 +56,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include <type_traits>
 
@@ -2341,4 +2342,56 @@ extern "C" int jb_attn_mass(const jb_attn_args* a, void* stream) { return kvq::d
 extern "C" size_t jb_attn_workspace_bytes(const jb_attn_args* a) {
   if (kvq::validate_attn(a, false) != KVQ_OK && kvq::validate_attn(a, true) != KVQ_OK) return SIZE_MAX;
   return kvq::plan_workspace(kvq::plan_attn(a, kvq::device_cus()));
+}
+
+// ---------------- the forward pass without allocation ----------------
+// For callers that cannot allocate device memory (code under graph capture, serving loops
+// that forbid it): the split partials or few-query records go to a fixed array in device
+// memory, one copy per device, which the library holds until the process ends.
+static __device__ __align__(256) unsigned char scratch[JB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// The current device's address of `scratch` (looked up on the first call on that device;
+// the array's name is a host-side stand-in, never passed to a kernel).
+int scratch_on_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return KVQ_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return KVQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return KVQ_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+}  // namespace
+
+extern "C" int jb_attn_fwd_noalloc(const jb_attn_args* a, void* stream) {
+  const int st = kvq::validate_attn(a, false);
+  if (st) return st;
+  const size_t need = kvq::plan_workspace(kvq::plan_attn(a, kvq::device_cus()));
+  if (need > (size_t)JB_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+  jb_attn_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (need > 0) {
+    void* ptr = nullptr;
+    const int s2 = scratch_on_device(&ptr);
+    if (s2) return s2;
+    b.workspace = ptr;
+    b.workspace_bytes = JB_NOALLOC_SCRATCH_BYTES;
+  }
+  return kvq::dispatch<false>(&b, stream);
 }

@@ -21,8 +21,10 @@ KVQ_ROLE_KEY, KVQ_ROLE_VALUE = 0, 1
 JB_CORR_NONE, JB_CORR_TAYLOR, JB_CORR_EXACT = 0, 1, 2
 
 EXPORTS = ("kvq_chunk_pad", "kvq_window_elems", "kvq_pack", "jb_attn_fwd", "jb_attn_mass",
-           "jb_attn_fwd_batch", "jb_attn_mass_batch", "jb_attn_workspace_bytes", "kvq_status_str")
+           "jb_attn_fwd_batch", "jb_attn_mass_batch", "jb_attn_workspace_bytes", "kvq_status_str",
+           "jb_attn_fwd_noalloc")
 KVQ_BATCH_MAX = 8
+JB_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class KvqError(RuntimeError):
@@ -92,7 +94,7 @@ def _load():
                              ctypes.POINTER(KvqFormat), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.kvq_pack.restype = ctypes.c_int
-    for fn in ("jb_attn_fwd", "jb_attn_mass"):
+    for fn in ("jb_attn_fwd", "jb_attn_mass", "jb_attn_fwd_noalloc"):
         getattr(lib, fn).argtypes = [ctypes.POINTER(JbAttnArgs), ctypes.c_void_p]
         getattr(lib, fn).restype = ctypes.c_int
     for fn in ("jb_attn_fwd_batch", "jb_attn_mass_batch"):
@@ -196,6 +198,12 @@ def make_args(q, k_cur, v_cur, k_window, v_window, chunk_len, n_chunks, k_fmt, v
 
 def jb_attn_fwd(args: JbAttnArgs, stream=None):
     _check("jb_attn_fwd", _lib.jb_attn_fwd(ctypes.byref(args), _stream(stream)))
+
+
+def jb_attn_fwd_noalloc(args: JbAttnArgs, stream=None):
+    """jb_attn_fwd without allocation: the library's per-device scratch array replaces the
+    workspace (args.workspace is ignored)."""
+    _check("jb_attn_fwd_noalloc", _lib.jb_attn_fwd_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 def jb_attn_mass(args: JbAttnArgs, stream=None):

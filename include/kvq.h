@@ -228,6 +228,21 @@ int jb_attn_mass_batch(const jb_attn_args* calls, int32_t n_calls, void* stream)
  * SIZE_MAX when the arguments are invalid (jb_attn_fwd would return a negative status). */
 size_t jb_attn_workspace_bytes(const jb_attn_args* a);
 
+/* The forward pass of jb_attn_fwd for callers that cannot allocate device memory (code under
+ * graph capture, serving loops or harnesses that forbid allocation): it calls no allocator.
+ * The split partials or few-query records that jb_attn_fwd keeps in the caller's workspace
+ * go to a fixed array of JB_NOALLOC_SCRATCH_BYTES bytes in device memory instead, one per
+ * device the library runs on, held until the process ends; a->workspace and
+ * a->workspace_bytes are ignored. Results equal jb_attn_fwd's with a workspace of
+ * jb_attn_workspace_bytes. Errors: those of jb_attn_fwd, and KVQ_ERR_WORKSPACE when the
+ * call would need more than JB_NOALLOC_SCRATCH_BYTES (jb_attn_workspace_bytes reports the
+ * need; nothing is launched). Every call on one device shares that device's array, and
+ * nothing in it needs to start at zero (each call writes every record it reads): calls
+ * that may overlap in time on one device (other streams or host threads) race on it and
+ * must be serialized by the caller. */
+#define JB_NOALLOC_SCRATCH_BYTES (64u << 20)
+int jb_attn_fwd_noalloc(const jb_attn_args* a, void* stream);
+
 /* Static description of a status code. */
 const char* kvq_status_str(int status);
 

@@ -34,22 +34,53 @@ CORR_NAMES = {0: "none", 1: "taylor", 2: "exact"}
 KERNEL_SOURCE = os.path.join(ROOT, "bit_kv_cache_kvq_amd", "csrc", "attn.hip")
 
 
+# Further workloads timed after the headline (attention kernel only, per-launch HIP events):
+# name -> (workload, replacements, correction)
+OTHERS = {
+    "tiny": ("tiny", {}, 1),
+    "c24": ("c24", {}, 1),
+    "c40_perch": ("c40_perch", {}, 1),
+    "long": ("long", {}, 1),
+    "c40_int4": ("c40", {"bits": 4}, 1),
+    "c40_q16": ("c40", {"n_q": 16}, 1),
+    "c40_tgroup32": ("c40_tgroup", {"group": 32}, 1),
+    "c40_tgroup64": ("c40_tgroup", {"group": 64}, 1),
+    "c40_exact": ("c40", {}, 2),
+}
+OTHER_LAUNCHES = 10
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile():
-    """HBM bytes per launch from the committed counter summary, if it describes this kernel."""
+def counters_from_profile():
+    """HBM bytes per launch and matrix-core / VALU busy fractions from the committed counter
+    summary, if it describes this kernel source (else an empty dict)."""
     try:
         txt = open(TRAFFIC_FILE).read()
     except OSError:
-        return None
+        return {}
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", txt)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
-        return None
-    return float(m_bytes.group(1))
+    if not m_hash or m_hash.group(1) != kernel_source_hash():
+        return {}
+    out = {}
+    for key, name in (("hbm_bytes_per_launch", "traffic"), ("mfma_busy", "mfma_busy"), ("valu_busy", "valu_busy")):
+        m = re.search(key + r":\s*([0-9.eE+]+)", txt)
+        if m:
+            out[name] = float(m.group(1))
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def gran_text(w, gran):
@@ -80,11 +111,13 @@ def cpu_baseline(w, x, heads, kf_o, vf_o, correction="taylor"):
     import oracle
     from oracle.quant import pack_window
 
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        blas = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        blas = affinity
+    threads = min(blas, affinity)  # the BLAS threads that do the oracle's matrix products
     xs = {k: np.stack([v[b, h] for (b, h) in heads])[None] for k, v in x.items()}
     cache = oracle.attention.quantize_cache(xs["k_cache"], xs["v_cache"], w.chunk_len, kf_o, vf_o)
     t0 = time.perf_counter()
@@ -95,10 +128,68 @@ def cpu_baseline(w, x, heads, kf_o, vf_o, correction="taylor"):
                                          cache=cache)
     dt = time.perf_counter() - t0
     flops = 4.0 * w.n_q * (w.n_c + w.n_r) * w.d * len(heads)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "affinity_cores": affinity,
+            "blas_threads": int(blas), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{len(heads)} of {w.bh} heads, all {w.n_q} query rows: float64 attention over the "
                       f"dequantized window + current chunk, plus float32-contract packing of the current "
                       f"chunk's K and V ({dt:.1f} s)"}, (O, PS, PR)
+
+
+def measure_other(key, launches=OTHER_LAUNCHES, warmup=3):
+    """Time one further workload's attention call (the whole call: split, merge or decode
+    kernels included) with per-launch HIP events on its stream; median and min launch."""
+    import numpy as np
+    import torch
+
+    from bit_kv_cache_kvq_amd import kvq, synth
+
+    name, repl, correction = OTHERS[key]
+    w = synth.WORKLOADS[name].replace(**repl)
+    x = synth.draw_all(w)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    kf = kvq.KvqFormat.make(w.bits, w.k_granularity, w.group, True, "key")
+    vf = kvq.KvqFormat.make(w.bits, w.v_granularity, w.group, True, "value")
+    q, kr, vr = dev(x["q"]), dev(x["k_cur"]), dev(x["v_cur"])
+    kwin = kvq.pack_window(dev(x["k_cache"]), w.chunk_len, kf)
+    vwin = kvq.pack_window(dev(x["v_cache"]), w.chunk_len, vf)
+    del x
+    o = torch.empty((w.B, w.H, w.n_q, w.d), dtype=torch.float32, device="cuda")
+    ms = torch.empty((w.B, w.H, w.n_q), dtype=torch.float32, device="cuda")
+    mr = torch.empty_like(ms)
+    a = kvq.make_args(q, kr, vr, kwin, vwin, w.chunk_len, w.n_chunks, kf, vf, o=o, mass_s=ms, mass_r=mr,
+                      correction=correction)
+    ws = kvq.attach_workspace(a)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        kvq.jb_attn_fwd(a, stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        kvq.jb_attn_fwd(a, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    med = float(np.median(t))
+    cache_bytes = sum(v.numel() * v.element_size() for v in (*kwin, *vwin))
+    algo_bytes = cache_bytes + 3 * w.bh * w.n_q * w.d * 2 + w.bh * w.n_q * (w.d + 2) * 4
+    decode = w.n_q <= 32 and w.k_granularity == "token" and correction != 2 and a.workspace_bytes > 0
+    rec = {"workload": f"{w.name} B={w.B} H={w.H} n_q={w.n_q} window {w.n_chunks}x{w.chunk_len} INT{w.bits} "
+                       f"K {gran_text(w, w.k_granularity)} correction={CORR_NAMES[correction]}",
+           "attn_ms_median": round(med, 5), "attn_ms_min": round(float(t.min()), 5),
+           "attn_ms_mean": round(float(t.mean()), 5), "launches": launches,
+           "path": "decode" if decode else ("split" if a.workspace_bytes > 0 else "main"),
+           "TFLOPs": round(w.flops() / (med * 1e-3) / 1e12, 2)}
+    if decode:
+        gbs = algo_bytes / (med * 1e-3) / 1e9
+        rec.update({"bound": "hbm", "GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    else:
+        rec.update({"bound": "mfma", "frac": round(w.flops() / (med * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)})
+    del ws, q, kr, vr, kwin, vwin, o, ms, mr
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -121,6 +212,9 @@ def main():
                          "launch (jb_attn_fwd_batch) when above 1")
     ap.add_argument("--group", type=int, default=0,
                     help="replace the workload's group size (channels per group for group-wise keys and values)")
+    ap.add_argument("--others", default=",".join(OTHERS),
+                    help="comma-separated list of further workloads whose attention kernel is timed after the "
+                         "headline (reported under 'workloads'); 'none' skips them")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="only run a device copy of this many MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -215,7 +309,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = float(np.mean([e0.elapsed_time(e1) for (e0, e1, _) in evs]))
+    attn_all = np.array([e0.elapsed_time(e1) for (e0, e1, _) in evs])
+    attn_ms = float(attn_all.mean())
     pack_ms = float(np.mean([e1.elapsed_time(e2) for (_, e1, e2) in evs]))
     # algorithmic bytes of the two packs: the chunk's bf16 keys and values read once, their
     # codes, steps and zero points written once
@@ -231,8 +326,9 @@ def main():
               and nl == 1)
     value = flops / (ms_step * 1e-3) / 1e12
     # the committed counters describe one c40 launch of this kernel source
-    traffic = traffic_from_profile() if (w.name == "c40" and nl == 1 and w.bits == 2 and args.correction == 1
-                                         and not args.nq and not args.no_workspace) else None
+    ctr = counters_from_profile() if (w.name == "c40" and nl == 1 and w.bits == 2 and args.correction == 1
+                                      and not args.nq and not args.no_workspace) else {}
+    traffic = ctr.get("traffic")
 
     rec = {
         "metric": METRIC,
@@ -254,6 +350,8 @@ def main():
                    "parallelism": "none (1 GPU)", "split_workspace_bytes": a.workspace_bytes, "layers": nl,
                    "batched_launch": nl > 1},
         "attn_ms": round(attn_ms, 4),
+        "attn_ms_median": round(float(np.median(attn_all)), 4),
+        "attn_ms_min": round(float(attn_all.min()), 4),
         "cache_GBps": round(cache_bytes / (attn_ms * 1e-3) / 1e9, 2),
         "window_memory": window_memory(w),
         "cache_frac_hbm": round(cache_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
@@ -265,7 +363,8 @@ def main():
                      {"bound": "hbm", "achieved": round(algo_bytes / (attn_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(algo_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
         | {"traffic": (round(traffic) if traffic is not None else None),
-           "algorithmic_bytes": algo_bytes, "kernel_source_sha256_16": kernel_source_hash()},
+           "algorithmic_bytes": algo_bytes, "kernel_source_sha256_16": kernel_source_hash(),
+           "mfma_busy": ctr.get("mfma_busy"), "valu_busy": ctr.get("valu_busy")},
         "path": "decode" if decode else ("batched" if nl > 1 else "main"),
     }
     if args.cpu_heads > 0:
@@ -279,6 +378,19 @@ def main():
         err = np.abs(og - O)
         rec["cpu_baseline"] = base
         rec["parity_on_sample"] = {"max_err_over_rms": float(err.max() / rms), "mean_err_over_rms": float(err.mean() / rms)}
+    others = [k for k in args.others.split(",") if k and k != "none"]
+    if others:
+        del layers, L0, q, kr, vr, kwin, vwin, o, knext, vnext, a, x
+        torch.cuda.empty_cache()
+        rec["workloads"] = {}
+        for k in others:
+            if k not in OTHERS:
+                print(f"unknown workload {k!r} (known: {', '.join(OTHERS)})", file=sys.stderr)
+                sys.exit(2)
+            t_o = time.perf_counter()
+            rec["workloads"][k] = measure_other(k)
+            print(f"# {k}: {rec['workloads'][k]['attn_ms_median']} ms ({time.perf_counter() - t_o:.1f} s)",
+                  file=sys.stderr, flush=True)
     print(json.dumps(rec), flush=True)
 
 

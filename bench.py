@@ -40,6 +40,7 @@ OTHERS = {
     "tiny": ("tiny", {}, 1),
     "c24": ("c24", {}, 1),
     "c40_perch": ("c40_perch", {}, 1),
+    "c40_perch_span": ("c40_perch_span", {}, 1),
     "long": ("long", {}, 1),
     "c40_int4": ("c40", {"bits": 4}, 1),
     "c40_q16": ("c40", {"n_q": 16}, 1),

@@ -276,7 +276,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   constexpr int NG = TG > 0 ? D / TG : 1;
   constexpr int KPG = TG > 0 ? TG / 32 : 1;
   constexpr int NB = (TG > 0 && 6 * NG + 3 > 16) ? 2 : 1;
-  static_assert(TG == 0 || (!PERCH && !EXACT && TG % 32 == 0 && TG < D && NG <= kNS), "group-wise options");
+  static_assert(TG == 0 || (!PERCH && TG % 32 == 0 && TG < D && NG <= kNS), "group-wise options");
   constexpr int HALF = D / 2;
   constexpr int KSTEPS = D / 32;  // int8 K-steps of 32 channels
   constexpr int CBLK = D / 32;    // 32-channel output blocks
@@ -366,6 +366,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // -m, plus the key group's constant c_grp (per-channel keys), into query slots 8, 9.
   float c_grp = 0.f;
   float ex2 = 0.f, ex3 = 0.f, ex4 = 0.f;  // exact correction, per-token keys (log2 units)
+  float exg[3][NG];                        // the same per channel group (group-wise keys)
   auto write_mslot = [&]() KVQ_INLINE {
     _Float16 mh = (_Float16)0.f, ml = (_Float16)0.f;
     split16(c_grp - (m_run == -INFINITY ? 0.f : m_run), mh, ml);
@@ -423,7 +424,27 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       }
     qs += __shfl_xor(qs, 32);
     const float G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
-    if constexpr (EXACT && !PERCH) {
+    if constexpr (EXACT && TG > 0) {
+      // group-wise keys: the same series per channel group g, with the group's step
+      // Delta_jg and moments M_n^g = sum over g's channels of (s q'_c / 2)^2n (this lane's
+      // K-steps of group g hold half of its channels; the partner lane the other half)
+#pragma unroll
+      for (int g = 0; g < NG; g++) {
+        float m2 = 0.f, m3 = 0.f, m4 = 0.f;
+#pragma unroll
+        for (int kk = g * KPG; kk < (g + 1) * KPG; kk++)
+#pragma unroll
+          for (int i = 0; i < 16; i++) {
+            const float y = 0.5f * p.s * qv[16 * kk + i], u = y * y, u2 = u * u;
+            m2 += u2;
+            m3 = fmaf(u2, u, m3);
+            m4 = fmaf(u2, u2, m4);
+          }
+        exg[0][g] = (m2 + xor32(m2)) * (1.f / 180.f) * kLog2e;
+        exg[1][g] = (m3 + xor32(m3)) * (1.f / 2835.f) * kLog2e;
+        exg[2][g] = (m4 + xor32(m4)) * (1.f / 37800.f) * kLog2e;
+      }
+    } else if constexpr (EXACT && !PERCH) {
       // b(Delta) = sum_c log_sinhc(s q'_c Delta / 2) = sum_n c_n M_n Delta^2n with
       // M_n = sum_c (s q'_c / 2)^2n: the n = 1 term is G's, n = 2..4 enter the logits
       float m2 = 0.f, m3 = 0.f, m4 = 0.f;
@@ -1146,6 +1167,23 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     if constexpr (decltype(k_c)::value == kCached && TG > 0) {
 #pragma unroll
       for (int v = 0; v < 16; v++) x[v] = fmaf(a_st, __int_as_float(sqh[SET][v]), cb[SET][v]);
+      if constexpr (EXACT) {
+        // the exact correction's terms past the second order, per channel group:
+        // -b gains Delta_g^4 (c2 M2^g - Delta_g^2 (c3 M3^g - Delta_g^2 c4 M4^g))
+        const _Float16* dkg = reinterpret_cast<const _Float16*>(&sm.prm[slot].dka[0][0]);
+#pragma unroll
+        for (int g = 0; g < NG; g++)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; v4++) {
+            const f16x4 d4 = *reinterpret_cast<const f16x4*>(&dkg[g * kBN + 32 * mb + 8 * v4 + 4 * h]);
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+              const float dd = (float)d4[b], u = dd * dd;
+              const float t = fmaf(-u, fmaf(-u, exg[2][g], exg[1][g]), exg[0][g]);
+              x[4 * v4 + b] = fmaf(u * u, t, x[4 * v4 + b]);
+            }
+          }
+      }
     } else if constexpr (decltype(k_c)::value == kCached && PERCH) {
 #pragma unroll
       for (int v = 0; v < 16; v++) x[v] = fmaf(a_ch, (float)sqh[SET][v], cb[SET][v]);
@@ -1442,13 +1480,13 @@ struct BatchParams {
   int n;
 };
 
-template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT, int TG = 0>
 __global__ __launch_bounds__(kThreads) void jb_attn_batch_kernel(const BatchParams bp) {
   int c = 0;
   while (c + 1 < bp.n && (int)blockIdx.x >= bp.start[c + 1]) c++;
   const int wg = (int)blockIdx.x - bp.start[c];
   if (wg >= bp.grid[c]) return;
-  attn_body<D, BITS, MASS_ONLY, PERCH, EXACT>(bp.p[c], wg, bp.grid[c]);
+  attn_body<D, BITS, MASS_ONLY, PERCH, EXACT, TG>(bp.p[c], wg, bp.grid[c]);
 }
 
 // ---------------- few queries: one wave per share of a head's cached tiles ----------------
@@ -2234,6 +2272,17 @@ int dispatch(const jb_attn_args* a, void* stream) {
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool perch = a->k_fmt.granularity == KVQ_PER_CHANNEL;
+  if (a->k_fmt.granularity == KVQ_PER_TOKEN_GROUP && a->correction == JB_CORR_EXACT && a->n_chunks > 0) {
+    const bool i2 = a->k_fmt.bits == 2;
+    if (a->d == 64)
+      return i2 ? launch_attn<64, 2, MASS_ONLY, false, true, 32>(a, pl, s)
+                : launch_attn<64, 4, MASS_ONLY, false, true, 32>(a, pl, s);
+    if (a->k_fmt.group == 32)
+      return i2 ? launch_attn<128, 2, MASS_ONLY, false, true, 32>(a, pl, s)
+                : launch_attn<128, 4, MASS_ONLY, false, true, 32>(a, pl, s);
+    return i2 ? launch_attn<128, 2, MASS_ONLY, false, true, 64>(a, pl, s)
+              : launch_attn<128, 4, MASS_ONLY, false, true, 64>(a, pl, s);
+  }
   if (a->k_fmt.granularity == KVQ_PER_TOKEN_GROUP) {
     const bool i2 = a->k_fmt.bits == 2;
     if (a->d == 64)
@@ -2267,7 +2316,7 @@ int dispatch(const jb_attn_args* a, void* stream) {
   return perch ? launch_attn<64, 4, MASS_ONLY, true>(a, pl, s) : launch_attn<64, 4, MASS_ONLY, false>(a, pl, s);
 }
 
-template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT>
+template <int D, int BITS, bool MASS_ONLY, bool PERCH, bool EXACT, int TG = 0>
 int launch_batch(const jb_attn_args* calls, int n, hipStream_t st) {
   // One split count S for the whole batch, chosen as for a single call but over the
   // workgroups of all calls: rounds of the device times the longest share. It is used
@@ -2288,7 +2337,7 @@ int launch_batch(const jb_attn_args* calls, int n, hipStream_t st) {
     next += ((long long)bp.grid[c] + 7) / 8 * 8;
     if (next > 0x7FFFFFFFLL) return KVQ_ERR_SHAPE;
   }
-  jb_attn_batch_kernel<D, BITS, MASS_ONLY, PERCH, EXACT><<<(unsigned)next, kThreads, 0, st>>>(bp);
+  jb_attn_batch_kernel<D, BITS, MASS_ONLY, PERCH, EXACT, TG><<<(unsigned)next, kThreads, 0, st>>>(bp);
   if (S > 1) {
     constexpr int G = MASS_ONLY ? 1 : D / 4;
     for (int c = 0; c < n; c++) {
@@ -2308,6 +2357,24 @@ int dispatch_batch(const jb_attn_args* calls, int n, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool perch = a0.k_fmt.granularity == KVQ_PER_CHANNEL;
   const bool exact = a0.correction == JB_CORR_EXACT;
+  if (a0.k_fmt.granularity == KVQ_PER_TOKEN_GROUP) {
+    // group-wise keys and values: one group size for the batch (checked by validate_batch)
+    const bool i2 = a0.k_fmt.bits == 2;
+#define KVQ_TG_BATCH(EX)                                                                                  \
+  if (a0.d == 64)                                                                                         \
+    return i2 ? launch_batch<64, 2, MASS_ONLY, false, EX, 32>(calls, n, s)                                \
+              : launch_batch<64, 4, MASS_ONLY, false, EX, 32>(calls, n, s);                               \
+  if (a0.k_fmt.group == 32)                                                                               \
+    return i2 ? launch_batch<128, 2, MASS_ONLY, false, EX, 32>(calls, n, s)                               \
+              : launch_batch<128, 4, MASS_ONLY, false, EX, 32>(calls, n, s);                              \
+  return i2 ? launch_batch<128, 2, MASS_ONLY, false, EX, 64>(calls, n, s)                                 \
+            : launch_batch<128, 4, MASS_ONLY, false, EX, 64>(calls, n, s);
+    if (exact) {
+      KVQ_TG_BATCH(true)
+    }
+    KVQ_TG_BATCH(false)
+#undef KVQ_TG_BATCH
+  }
 #define KVQ_BATCH_CASE(D_, B_)                                                                             \
   if (a0.d == D_ && a0.k_fmt.bits == B_) {                                                                 \
     if (perch)                                                                                             \

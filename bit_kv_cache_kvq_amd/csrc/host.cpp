@@ -73,10 +73,9 @@ int validate_attn(const jb_attn_args* a, bool mass_only) {
   if (vf.bits != kf.bits) return KVQ_ERR_UNSUPPORTED;
   if (kf.role != KVQ_ROLE_KEY || vf.role != KVQ_ROLE_VALUE) return KVQ_ERR_UNSUPPORTED;
   if (kf.granularity == KVQ_PER_TOKEN_GROUP || vf.granularity == KVQ_PER_TOKEN_GROUP) {
-    // group-wise keys and values together, one group size, second-order correction
+    // group-wise keys and values together, one group size
     if (kf.granularity != vf.granularity || kf.group != vf.group) return KVQ_ERR_UNSUPPORTED;
     if ((kf.group != 32 && kf.group != 64) || kf.group >= a->d) return KVQ_ERR_UNSUPPORTED;
-    if (a->correction == JB_CORR_EXACT) return KVQ_ERR_UNSUPPORTED;
   } else {
     if (vf.granularity != KVQ_PER_TOKEN) return KVQ_ERR_UNSUPPORTED;
     if (kf.granularity != KVQ_PER_TOKEN && kf.granularity != KVQ_PER_CHANNEL) return KVQ_ERR_UNSUPPORTED;
@@ -136,9 +135,8 @@ int validate_batch(const jb_attn_args* calls, int n, bool mass_only) {
     const int st = validate_attn(&calls[c], mass_only);
     if (st) return st;
     const jb_attn_args& a = calls[c];
-    if (a.k_fmt.granularity == KVQ_PER_TOKEN_GROUP) return KVQ_ERR_UNSUPPORTED;  // single calls only
     if (a.d != a0.d || a.k_fmt.bits != a0.k_fmt.bits || a.k_fmt.granularity != a0.k_fmt.granularity ||
-        (a.k_fmt.granularity == KVQ_PER_CHANNEL && a.k_fmt.group != a0.k_fmt.group) ||
+        (a.k_fmt.granularity != KVQ_PER_TOKEN && a.k_fmt.group != a0.k_fmt.group) ||
         (a.correction == JB_CORR_EXACT) != (a0.correction == JB_CORR_EXACT))
       return KVQ_ERR_UNSUPPORTED;
   }

@@ -93,6 +93,10 @@ WORKLOADS = {
     "c40": Workload("c40", B=1, H=40, d=128, n_q=4680, chunk_len=4680, n_chunks=8),
     "c40_perch": Workload("c40_perch", B=1, H=40, d=128, n_q=4680, chunk_len=4680, n_chunks=8,
                           k_dist="t3", k_granularity="channel", group=128),
+    # the per-channel workload with the window packed as one sequence: key groups of 128
+    # tokens run over the whole window, across the boundaries of its 8 chunks (same data)
+    "c40_perch_span": Workload("c40_perch_span", B=1, H=40, d=128, n_q=4680, chunk_len=37440, n_chunks=1,
+                               k_dist="t3", k_granularity="channel", group=128),
     # the c40 shape with group-wise per-token keys and values (32 channels per group)
     "c40_tgroup": Workload("c40_tgroup", B=1, H=40, d=128, n_q=4680, chunk_len=4680, n_chunks=8,
                            k_granularity="token_group", group=32),

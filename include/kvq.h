@@ -69,7 +69,9 @@ enum { JB_CORR_NONE = 0, JB_CORR_TAYLOR = 1, JB_CORR_EXACT = 2 };
  *                   granularity; pair j of a token covers channels [j*group, (j+1)*group)
  *                   of the stored (rotated) basis; pad tokens hold 0.
  *   KVQ_PER_CHANNEL [B, H, n_chunks*ceil(chunk_len/group), d]; groups restart at each
- *                   chunk's first token, the last group of a chunk may be short.
+ *                   chunk's first token, the last group of a chunk may be short. Groups that
+ *                   span the boundaries of the chunks a stream produced are had by packing
+ *                   those chunks as one (chunk_len = their total, n_chunks = 1).
  *
  * Quantizer (paper §3, Eq. (1)), one fixed float32 operation order, so results are
  * reproducible bit for bit: y = H x in float32 (butterfly stages h = 1, 2, ..., d/2,
@@ -136,7 +138,8 @@ int kvq_pack(const uint16_t* x, int32_t B, int32_t H, int32_t n, int32_t d, cons
  * Per-channel keys evaluate it once per query and key group (relative error of each
  * channel's term below 1e-6). Per-token keys evaluate its power series in Delta_j through
  * Delta_j^8 (the omitted terms are below (max_c x)^8 sum_c x^2 / 467775 nats: 2e-6 per
- * channel at x = 1; the series does not converge past x = pi). */
+ * channel at x = 1; the series does not converge past x = pi); group-wise per-token keys
+ * the same series per channel group, in that group's step Delta_j,grp. */
 typedef struct {
   int32_t B, H, d;            /* d in {64, 128}; the same H for queries and keys */
   int32_t n_q;                /* current-chunk queries, >= 1 */
@@ -154,7 +157,7 @@ typedef struct {
   const uint16_t* v_zero;
   kvq_format k_fmt, v_fmt;    /* same bits; k: KEY per token or per channel with v: VALUE per
                                  token; or both KVQ_PER_TOKEN_GROUP with one group (32 or
-                                 64 < d), correction not JB_CORR_EXACT */
+                                 64 < d) */
   float softmax_scale;        /* s; 0 selects 1/sqrt(d) */
   int32_t correction;         /* JB_CORR_NONE, JB_CORR_TAYLOR or JB_CORR_EXACT */
   float* o;                   /* fp32 [B, H, n_q, d]: required by fwd, ignored by mass */
@@ -197,7 +200,7 @@ int jb_attn_mass(const jb_attn_args* a, void* stream);
  * call's workspace holds its partials for that count; otherwise
  * no call is split, and each computes exactly what jb_attn_fwd (jb_attn_mass) would for
  * it unsplit. Calls must agree on d, bits, key
- * granularity (and group; KVQ_PER_TOKEN_GROUP is for single calls only: KVQ_ERR_UNSUPPORTED),
+ * granularity (and group, for per-channel and group-wise formats),
  * and on whether correction is JB_CORR_EXACT; shapes, windows,
  * rotation flags and signs, softmax scale and the other correction modes may differ.
  * calls points to n_calls host structs, 1 <= n_calls <= KVQ_BATCH_MAX.

@@ -131,7 +131,7 @@ def test_attn_validation_without_launch(kvq):
     tg = lambda g, role, d=128: kvq.KvqFormat.make(2, "token_group", g, True, role)
     assert fwd(args(k_fmt=tg(32, "key"))) == -3                                  # values must be group-wise too
     assert fwd(args(k_fmt=tg(32, "key"), v_fmt=tg(64, "value"))) == -3          # one group size
-    assert fwd(args(k_fmt=tg(32, "key"), v_fmt=tg(32, "value"), correction=2)) == -3  # exact: per token/channel only
+    assert fwd(args(k_fmt=tg(32, "key"), v_fmt=tg(32, "value"), correction=2, o=None)) == -1  # exact: the format passes
     assert fwd(args(d=64, k_fmt=tg(64, "key"), v_fmt=tg(64, "value"))) == -3   # a group narrower than d
     assert fwd(args(k_fmt=tg(32, "key"), v_fmt=tg(32, "value"), o=None)) == -1  # the format passes
     assert fwd(args(o=None)) == -1
@@ -171,7 +171,9 @@ def test_batch_validation_without_launch(kvq):
     assert batch([args()] * 9) == -2                                   # more than KVQ_BATCH_MAX
     assert batch([args(), args(o=None)]) == -1                        # a call's own validation
     tgk, tgv = kvq.KvqFormat.make(2, "token_group", 32, True, "key"), kvq.KvqFormat.make(2, "token_group", 32, True, "value")
-    assert batch([args(k_fmt=tgk, v_fmt=tgv)]) == -3                   # group-wise: single calls only
+    assert batch([args(k_fmt=tgk, v_fmt=tgv), args()]) == -3            # group-wise and per-token mixed
+    tgk64, tgv64 = kvq.KvqFormat.make(2, "token_group", 64, True, "key"), kvq.KvqFormat.make(2, "token_group", 64, True, "value")
+    assert batch([args(k_fmt=tgk, v_fmt=tgv), args(k_fmt=tgk64, v_fmt=tgv64)]) == -3  # two group sizes
     assert batch([args(), args(d=64, k_fmt=kvq.KvqFormat.make(2, "token", 128, True, "key"))]) == -3
     assert batch([args(), args(correction=2)]) == -3                  # exact and Taylor mixed
     assert batch([args(), args(k_fmt=kvq.KvqFormat.make(4, "token", 128, True, "key"),

@@ -120,6 +120,38 @@ def test_workload_sampled_rows(name, nrows):
         assert_mass_close(PS[b, h][None, None], PR[b, h][None, None], PSr, PRr, f"long head {head}")
 
 
+def test_per_channel_groups_spanning_chunks():
+    """Per-channel key groups that span chunk boundaries: the c40_perch window (8 chunks of
+    4,680 tokens) packed as one sequence, so its 128-token groups run across the chunk
+    boundaries (293 groups, the last of 64 tokens, instead of 37 per chunk). The inputs are
+    c40_perch's own. Codes bit-exact; every row of one head and sampled rows of two more."""
+    import oracle as orc
+    w = synth.WORKLOADS["c40_perch_span"]
+    assert w.n_c == synth.WORKLOADS["c40_perch"].n_c and w.n_chunks == 1
+    print("attn c40_perch_span: window packed as one sequence", flush=True)
+    x = synth.draw_all(w)
+    kvq = _kvq()
+    kf, _ = lib_formats(w)
+    okf, _ = oracle_formats(w)
+    head = [(0, 3)]
+    xs = np.stack([x["k_cache"][0, 3]])[None]
+    words, scale, zero = orc.quant.pack_window(xs, w.chunk_len, okf)
+    kw = kvq.pack_window(dev(xs), w.chunk_len, kf)
+    assert scale.shape[2] == 293
+    np.testing.assert_array_equal(kw[0].cpu().numpy().view(np.uint32), words)
+    np.testing.assert_array_equal(kw[1].cpu().numpy().view(np.uint16), scale.view(np.uint16))
+    np.testing.assert_array_equal(kw[2].cpu().numpy().view(np.uint16), zero.view(np.uint16))
+    O, PS, PR = run_gpu(x, w, masses=True)
+    Or, PSr, PRr = run_oracle(x, w, heads=head)
+    assert_attention_close(O[0, 3][None, None], Or, "c40_perch_span head (0, 3)")
+    assert_mass_close(PS[0, 3][None, None], PR[0, 3][None, None], PSr, PRr, "c40_perch_span head (0, 3)")
+    rows = np.sort(np.random.default_rng(9).choice(w.n_q, 48, replace=False))
+    heads = [(0, 17), (0, 38)]
+    Or, PSr, PRr = run_oracle(x, w, rows=rows, heads=heads)
+    assert_attention_close(_gather(O, heads, rows), Or, "c40_perch_span sampled")
+    assert_mass_close(_gather(PS, heads, rows), _gather(PR, heads, rows), PSr, PRr, "c40_perch_span sampled")
+
+
 # every row of a few full-size heads (head (0, 12) of c40 holds rows whose attention mass
 # sits a few binades below the first keys' maximum)
 FULL_HEADS = [("c40", (0, 12)), ("c40", (0, 31)), ("c24", (0, 5)), ("c40_perch", (0, 7))]
@@ -747,7 +779,10 @@ TGROUP = [
 
 
 @pytest.mark.parametrize("shape", TGROUP, ids=lambda s: "x".join(str(v) for v in s.values()))
-@pytest.mark.parametrize("bits,correction,had", [(2, 1, True), (4, 1, True), (2, 0, True), (2, 1, False)])
+# (the exact correction's series is used where x = s q'_c Delta / 2 stays well inside its
+# radius: rotated keys; un-rotated outlier channels put x past 2 in their group)
+@pytest.mark.parametrize("bits,correction,had", [(2, 1, True), (4, 1, True), (2, 0, True), (2, 1, False),
+                                                 (2, 2, True), (4, 2, True)])
 def test_token_group_all_rows(shape, bits, correction, had):
     w = synth.Workload("tgroup", **shape, bits=bits, k_granularity="token_group", seed=11)
     print(f"attn token_group {shape} bits={bits} c={correction} had={had}", flush=True)
@@ -771,6 +806,61 @@ def test_token_group_mass_only_and_unsplit():
     Or, _, _ = run_oracle(x, w)
     assert_attention_close(O1, Or, "token_group split")
     assert_attention_close(O0, Or, "token_group unsplit")
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_token_group_exact_separates_from_taylor(group):
+    """Group-wise keys with large x = s q'_c Delta_j,grp / 2 (a softmax scale of 0.2: x below
+    1.9, inside the series' radius pi): the exact and second-order corrections differ by
+    more than the tolerance, and the kernel follows the exact one."""
+    from oracle.attention import quantize_cache
+    w = synth.Workload("tgroup_x", B=1, H=2, d=128, n_q=96, chunk_len=128, n_chunks=2, k_granularity="token_group",
+                       group=group, seed=14)
+    scale = 0.2
+    print(f"attn token_group g{group} exact vs taylor (large steps)", flush=True)
+    x = synth.draw_all(w)
+    kf, vf = oracle_formats(w)
+    cache = quantize_cache(x["k_cache"], x["v_cache"], w.chunk_len, kf, vf)
+    q_rot_max = np.abs(oracle.hadamard.rotate_f64(synth.bf16_bits_to_f32(x["q"]).astype(np.float64))).max()
+    x_bound = scale * q_rot_max * cache["k_scale"].astype(np.float64).max() / 2
+    print(f"largest x at most {x_bound:.2f}", flush=True)
+    assert x_bound < 2.0
+    O2, PS2, PR2 = run_gpu(x, w, correction=2, scale=scale)
+    Ot, _, _ = run_oracle(x, w, correction="taylor", scale=scale)
+    Ox, PSx, PRx = run_oracle(x, w, correction="exact", scale=scale)
+    sep = np.abs(Ot - Ox).max() / np.sqrt((Ox ** 2).mean())
+    print(f"taylor vs exact separation {sep:.3e}", flush=True)
+    assert sep > 2e-2
+    assert_attention_close(O2, Ox, f"token_group g{group} exact")
+    assert_mass_close(PS2, PR2, PSx, PRx, f"token_group g{group} exact")
+
+
+@pytest.mark.parametrize("group,correction", [(32, 1), (64, 2), (32, 0)])
+def test_batched_calls_token_group(group, correction):
+    """jb_attn_fwd_batch with group-wise keys and values: shapes, windows and scales differ
+    between the calls; each call equals the same call run alone and unsplit bit for bit and
+    the oracle within the tolerance."""
+    kvq = _kvq()
+    calls, outs, keep, specs = [], [], [], []
+    for i, (shape, opt) in enumerate(BATCH_SHAPES[:3]):
+        w = synth.Workload("batchtg", **shape, k_granularity="token_group", group=group, seed=90 + i)
+        x = synth.draw_all(w)
+        a, out, kp = _prepare(x, w, correction=correction, scale=opt.get("scale", 0.0))
+        calls.append(a)
+        outs.append(out)
+        keep.append(kp)
+        specs.append((w, x, opt))
+    print(f"attn batch token_group g{group} c{correction}: {len(calls)} calls", flush=True)
+    kvq.jb_attn_fwd_batch(calls)
+    torch.cuda.synchronize()
+    for (w, x, opt), (o, ms, mr) in zip(specs, outs):
+        O, PS, PR = o.cpu().numpy(), ms.cpu().numpy(), mr.cpu().numpy()
+        Or, PSr, PRr = run_oracle(x, w, correction=CORR[correction], scale=opt.get("scale") or None)
+        assert_attention_close(O, Or, f"batch tg{group} {w.B}x{w.H}x{w.n_q}")
+        assert_mass_close(PS, PR, PSr, PRr, f"batch tg{group} {w.B}x{w.H}x{w.n_q}")
+        O1, PS1, _ = run_gpu(x, w, correction=correction, scale=opt.get("scale", 0.0), split=False)
+        np.testing.assert_array_equal(O, O1)
+        np.testing.assert_array_equal(PS, PS1)
 
 
 def test_token_group_c40_sampled_rows():

@@ -208,11 +208,8 @@ struct SmemSlots {
     uint32_t zv[kBN / 2];   // (-1024 - z^V) fp16 pairs, token pair (j, j+8) order
     uint32_t dvp[kBN / 2];  // (Delta^V_j, Delta^V_j+8) fp16 pairs
   };
-  // Group-wise keys and values (NG channel groups per token): bias operand slots 16..31,
-  // and one zero-point / step pair table per value channel group.
-  struct PSlotG : PSlot {
-    uint4 kb2[kBN][2];
-  };
+  // Group-wise keys and values (NG channel groups per token): one zero-point / step pair
+  // table per value channel group.
   template <int NG>
   struct ZSlotG {
     uint32_t zv[NG][kBN / 2];
@@ -225,9 +222,9 @@ struct SmemSlots {
 template <int D, bool PERCH = false, int TG = 0>
 struct Smem : SmemSlots<D> {
   using T = SmemSlots<D>;
-  using PS = std::conditional_t<(TG > 0), typename T::PSlotG, typename T::PSlot>;
+  using PS = typename T::PSlot;
   using ZS = std::conditional_t<(TG > 0), typename T::template ZSlotG<(TG > 0 ? D / TG : 1)>, typename T::ZSlot>;
-  alignas(16) typename T::KSlot k[3];
+  alignas(16) typename T::KSlot k[3];     // cached codes, or fp16 keys (group-wise, current)
   alignas(16) _Float16 v[3][D][T::VROW];  // value rows: fp16((code - z) Delta^V) or current values
   alignas(16) PS prm[3];
   alignas(16) ZS z[3];
@@ -269,13 +266,11 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   __shared__ Smem<D, PERCH, TG> sm;
   using SM = Smem<D, PERCH, TG>;
   // Group-wise keys and values (TG channels per group): NG (step, zero point) pairs per
-  // token; K-step kk of the int8 QK^T covers channels [32 kk, 32 kk + 32), so a group is
-  // KPG whole K-steps. The bias MFMA carries 3 fp16 slots (hi/lo cross terms) per group
-  // for the zero point and per group for the correction, plus -m and the mask: a second
-  // bias MFMA (slots 16..31) when that passes 16.
+  // token. Cached keys are dequantized to fp16 Delta_jg (code - z_jg) in the staging (each
+  // 16-channel unit lies in one group) and QK^T runs on fp16 MFMA against the rotated query
+  // split into fp16 hi + lo parts (two MFMAs per K-step, one fp32 accumulator); the bias
+  // MFMA carries the per-group correction (3 fp16 slots per group), -m and the mask.
   constexpr int NG = TG > 0 ? D / TG : 1;
-  constexpr int KPG = TG > 0 ? TG / 32 : 1;
-  constexpr int NB = (TG > 0 && 6 * NG + 3 > 16) ? 2 : 1;
   static_assert(TG == 0 || (!PERCH && TG % 32 == 0 && TG < D && NG <= kNS), "group-wise options");
   constexpr int HALF = D / 2;
   constexpr int KSTEPS = D / 32;  // int8 K-steps of 32 channels
@@ -319,8 +314,9 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
 
   // ---------------- query operands ----------------
   i32x4 qhi[KSTEPS], qlo[KSTEPS];  // int8 hi/lo of q_f (cached keys), or the bf16 query
+  // group-wise keys: the rotated query as fp16 hi + lo, in the staged key rows' channel order
+  f16x8 q16h[TG > 0 ? D / 16 : 1], q16l[TG > 0 ? D / 16 : 1];
   f16x8 qbias;                     // query operand of the bias MFMA
-  f16x8 qbias2 = {};               // group-wise keys: the second bias MFMA's (slots 16..31)
   float m_run = -INFINITY;         // reference max (log2 units); -inf until the first block
   float a_st = 0.f;                // A of this wave's stream
   // Rotated query q' = H q / sqrt(d) (or q) of this lane's half: channels HALF h + i.
@@ -377,19 +373,18 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     float qv[HALF];
     rotated_query(qv);
     if constexpr (TG > 0) {
-      // slot (kk, i) of half h takes channel 32 kk + 16 h + i (both halves' channels of a
-      // 32-channel block sit in one half of the rotation's layout: one exchange moves them)
-      float qn[HALF];
+      // position 16u + 2k + b of a staged key row holds channel 16u + k + 8b (the pair
+      // order of the code unpack); lane half h, K-step t reads positions HALF h + 8t ..
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk++)
+      for (int t = 0; t < D / 16; t++)
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int c0 = 32 * kk + i, c1 = c0 + 16, o = c0 / HALF;
-          const float recv = xor32(qv[(o == 0 ? c1 : c0) % HALF]);
-          qn[16 * kk + i] = h == o ? qv[(o == 0 ? c0 : c1) % HALF] : recv;
+        for (int e = 0; e < 8; e++) {
+          const int pp = 8 * t + e, c = 16 * (pp >> 4) + ((pp & 15) >> 1) + 8 * (pp & 1);
+          _Float16 hi_, lo_;
+          split16(qv[c], hi_, lo_);
+          q16h[t][e] = hi_;
+          q16l[t][e] = lo_;
         }
-#pragma unroll
-      for (int i = 0; i < HALF; i++) qv[i] = qn[i];
     }
     float ss = 0.f, mxa = 0.f;
 #pragma unroll
@@ -403,7 +398,6 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
     const float A = mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
     int qs = 0;
-    int qsg[NG] = {};  // group-wise keys: this half's sum of q_f over each group
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; kk++)
 #pragma unroll
@@ -415,7 +409,6 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           const int hi = (qf + 128) >> 8;
           const int lo = qf - (hi << 8);
           qs += qf;
-          if constexpr (TG > 0) qsg[kk / KPG] += qf;
           whi |= (uint32_t)(hi & 0xFF) << (8 * b);
           wlo |= (uint32_t)(lo & 0xFF) << (8 * b);
         }
@@ -426,20 +419,19 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     const float G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
     if constexpr (EXACT && TG > 0) {
       // group-wise keys: the same series per channel group g, with the group's step
-      // Delta_jg and moments M_n^g = sum over g's channels of (s q'_c / 2)^2n (this lane's
-      // K-steps of group g hold half of its channels; the partner lane the other half)
+      // Delta_jg and moments M_n^g = sum over g's channels of (s q'_c / 2)^2n (this lane
+      // holds channels HALF h + i, the partner lane the other half)
 #pragma unroll
       for (int g = 0; g < NG; g++) {
         float m2 = 0.f, m3 = 0.f, m4 = 0.f;
 #pragma unroll
-        for (int kk = g * KPG; kk < (g + 1) * KPG; kk++)
-#pragma unroll
-          for (int i = 0; i < 16; i++) {
-            const float y = 0.5f * p.s * qv[16 * kk + i], u = y * y, u2 = u * u;
-            m2 += u2;
-            m3 = fmaf(u2, u, m3);
-            m4 = fmaf(u2, u2, m4);
-          }
+        for (int i = 0; i < HALF; i++) {
+          if ((HALF * h + i) / TG != g) continue;
+          const float y = 0.5f * p.s * qv[i], u = y * y, u2 = u * u;
+          m2 += u2;
+          m3 = fmaf(u2, u, m3);
+          m4 = fmaf(u2, u2, m4);
+        }
         exg[0][g] = (m2 + xor32(m2)) * (1.f / 180.f) * kLog2e;
         exg[1][g] = (m3 + xor32(m3)) * (1.f / 2835.f) * kLog2e;
         exg[2][g] = (m4 + xor32(m4)) * (1.f / 37800.f) * kLog2e;
@@ -484,25 +476,20 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       for (int e = 3; e < 8; e++) qbias[e] = (_Float16)0.f;
     }
     if constexpr (TG > 0) {
-      // term t: zero point of group t (t < NG), correction of group t - NG; its three
-      // slots are k = 3t .. 3t+2 at bias slot k + 3 (k >= 8): 8, 9, 10 carry -m and the mask
-      _Float16 qsl[16 * NB];
+      // term t: the correction of group t, -s^2 |q'_t|^2 / 24 (times 64, log2 units); its
+      // three slots are k = 3t .. 3t+2 at bias slot k + 3 (k >= 8): 8, 9, 10 carry -m and
+      // the mask
+      _Float16 qsl[16];
 #pragma unroll
-      for (int k = 0; k < 16 * NB; k++) qsl[k] = (_Float16)0.f;
+      for (int k = 0; k < 16; k++) qsl[k] = (_Float16)0.f;
 #pragma unroll
-      for (int t = 0; t < 2 * NG; t++) {
-        float y;
-        if (t < NG) {
-          y = -A * (float)(qsg[t] + __shfl_xor(qsg[t], 32));
-        } else {
-          float sg = 0.f;
+      for (int t = 0; t < NG; t++) {
+        float sg = 0.f;
 #pragma unroll
-          for (int kk = (t - NG) * KPG; kk < (t - NG + 1) * KPG; kk++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) sg += qv[16 * kk + i] * qv[16 * kk + i];
-          sg += xor32(sg);
-          y = p.correction ? -(p.s * p.s * sg * (1.f / 24.f) * kLog2e) * kD2Scale : 0.f;
-        }
+        for (int i = 0; i < HALF; i++)
+          if ((HALF * h + i) / TG == t) sg += qv[i] * qv[i];
+        sg += xor32(sg);
+        const float y = p.correction ? -(p.s * p.s * sg * (1.f / 24.f) * kLog2e) * kD2Scale : 0.f;
         _Float16 yh, yl;
         split16(y, yh, yl);
         const int k0 = 3 * t;
@@ -513,10 +500,6 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
 #pragma unroll
       for (int e = 0; e < 8; e++) qbias[e] = h ? qsl[8 + e] : qsl[e];
       if (h) qbias[2] = (_Float16)(-kMaskLogit);
-      if constexpr (NB == 2) {
-#pragma unroll
-        for (int e = 0; e < 8; e++) qbias2[e] = h ? qsl[24 + e] : qsl[16 + e];
-      }
     }
     write_mslot();  // -m (hi, lo); 0 while m is unset
     if (lane == 0) sm.a_stream[wave] = A;
@@ -717,8 +700,10 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   uint32_t pk_dk = 0, pk_zk = 0;                 // key step / zero point of key tid & 63
   uint4 gpre = make_uint4(0, 0, 0, 0);           // per-channel keys: 16 bytes of the group rows
   uint32_t pz0 = 0, pz1 = 0, pd0 = 0, pd1 = 0;   // value zero points / steps of a token pair
-  // group-wise: the NG fp16 pairs of a token (groups 0, 1 in .x, groups 2, 3 in .y)
-  uint2 gk_d = make_uint2(0, 0), gk_z = make_uint2(0, 0);
+  // group-wise: the NG fp16 steps of key tid & 63 (groups 0, 1 in .x, groups 2, 3 in .y),
+  // and the step and zero point of this thread's 16-channel key unit
+  uint2 gk_d = make_uint2(0, 0);
+  uint32_t uk_d = 0, uk_z = 0;
   uint2 gv_z0 = make_uint2(0, 0), gv_z1 = make_uint2(0, 0), gv_d0 = make_uint2(0, 0), gv_d1 = make_uint2(0, 0);
   auto load_pairs = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t tok, uint32_t tok0) KVQ_INLINE -> uint2 {
     if constexpr (NG == 4) {
@@ -750,7 +735,10 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       if constexpr (TG > 0) {
         const uint32_t j = (uint32_t)(tid & (kBN - 1));
         gk_d = load_pairs(rs_ks, j, tok0);
-        gk_z = load_pairs(rs_kz, j, tok0);
+        const uint32_t un = (uint32_t)min(tid, KUNITS - 1);
+        const uint32_t pi = (un / (D / 16)) * NG + (un % (D / 16)) * 16 / TG;  // (token, group) pair
+        uk_d = __builtin_amdgcn_raw_buffer_load_b16(rs_ks, pi * 2u, tok0 * 2u * NG, 0);
+        uk_z = __builtin_amdgcn_raw_buffer_load_b16(rs_kz, pi * 2u, tok0 * 2u * NG, 0);
       } else if constexpr (!PERCH) {
         const uint32_t j = (uint32_t)(tid & (kBN - 1));
         pk_dk = __builtin_amdgcn_raw_buffer_load_b16(rs_ks, j * 2u, tok0 * 2u, 0);
@@ -804,10 +792,41 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           const uint32_t w0 = kpre[i].x, w1 = kpre[i].y;
           lo = make_uint4(w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu);
         }
-        if constexpr (PERCH)  // packed code slots
+        if constexpr (TG > 0) {
+          // fp16 Delta (code - z) of channels 16 ui + k (low half) and 16 ui + k + 8 (high)
+          // at positions 16 ui + 2k, + 1: (1024 + code) - (1024 + z) is exact in fp16
+          uint32_t a[8];
+          if constexpr (BITS == 2) {
+            const uint32_t w = kpre[i].x;
+#pragma unroll
+            for (int j = 0; j < 8; j++) a[j] = ((w >> (2 * j)) & 0x00030003u) | 0x64006400u;
+          } else {
+            const uint32_t w0 = kpre[i].x, w1 = kpre[i].y;
+            const uint32_t t0 = (w0 & 0xFFFFu) | (w1 << 16);
+            const uint32_t t1 = (w0 >> 16) | (w1 & 0xFFFF0000u);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+              a[j] = ((t0 >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+              a[4 + j] = ((t1 >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+            }
+          }
+          const float zf = half_bits_to_f32(uk_z);
+          const uint32_t zz = pack_f16x2(-1024.f - zf, -1024.f - zf);
+          const uint32_t dd = (uk_d & 0xFFFFu) | (uk_d << 16);
+          uint32_t res[8];
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            const f16x2 cz = __builtin_bit_cast(f16x2, a[j]) + __builtin_bit_cast(f16x2, zz);
+            res[j] = __builtin_bit_cast(uint32_t, cz * __builtin_bit_cast(f16x2, dd));
+          }
+          uint4* dst = reinterpret_cast<uint4*>(&ks.kr[tok][16 * ui]);
+          dst[0] = make_uint4(res[0], res[1], res[2], res[3]);
+          dst[1] = make_uint4(res[4], res[5], res[6], res[7]);
+        } else if constexpr (PERCH) {  // packed code slots
           *reinterpret_cast<uint4*>(&sm.kc(slot)[tok][16 * ui]) = lo;
-        else
+        } else {
           *reinterpret_cast<uint4*>(&ks.c[tok][16 * ui]) = lo;
+        }
       }
       // Delta_j A of each wave's stream; 0 for padding keys (their logit is set by the mask)
       if constexpr (PERCH) {
@@ -832,21 +851,19 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       }
       if constexpr (TG > 0) {
         if (wave == 0) {
-          // bias key operand: term t (zero point Delta z of group t, then Delta^2 / 64 of
-          // group t - NG) as (hi, hi, lo) at slots k = 3t.., slot k + 3 from k = 8 on;
-          // slots 8, 9 = 1 (the -m pair), 10 = the mask
+          // bias key operand: term t (Delta^2 / 64 of group t) as (hi, hi, lo) at slots
+          // k = 3t.., slot k + 3 from k = 8 on; slots 8, 9 = 1 (the -m pair), 10 = the mask
           const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
-          uint32_t ksl[8 * NB];
+          uint32_t ksl[8];
 #pragma unroll
-          for (int k = 0; k < 8 * NB; k++) ksl[k] = 0u;
+          for (int k = 0; k < 8; k++) ksl[k] = 0u;
           const uint32_t one = 0x3C00u;
           ksl[4] = one | (one << 16);
           if (lane < nv) {
 #pragma unroll
-            for (int t = 0; t < 2 * NG; t++) {
-              const int g = t < NG ? t : t - NG;
-              const float dk = half_bits_to_f32(pair_bits(gk_d, g));
-              const float x = t < NG ? dk * half_bits_to_f32(pair_bits(gk_z, g)) : dk * dk * (1.f / kD2Scale);
+            for (int t = 0; t < NG; t++) {
+              const float dk = half_bits_to_f32(pair_bits(gk_d, t));
+              const float x = dk * dk * (1.f / kD2Scale);
               _Float16 xh, xl;
               split16(x, xh, xl);
               const uint32_t hb = __builtin_bit_cast(uint16_t, xh), lb = __builtin_bit_cast(uint16_t, xl);
@@ -862,10 +879,6 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           }
           ps.kb[r][0] = make_uint4(ksl[0], ksl[1], ksl[2], ksl[3]);
           ps.kb[r][1] = make_uint4(ksl[4], ksl[5], ksl[6], ksl[7]);
-          if constexpr (NB == 2) {
-            ps.kb2[r][0] = make_uint4(ksl[8], ksl[9], ksl[10], ksl[11]);
-            ps.kb2[r][1] = make_uint4(ksl[12], ksl[13], ksl[14], ksl[15]);
-          }
         }
       } else if (PERCH && wave == 0) {
         // per-channel keys: the group terms ride on the query side (slots 8, 9)
@@ -1051,29 +1064,27 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
 
   // Key-side operands of block mb of tile U: the bias row and the key codes (cached) or
   // bf16 key rows (current), read from LDS ahead of their MFMAs.
-  uint4 kbop, kbop2 = make_uint4(0, 0, 0, 0);
+  uint4 kbop;
   i32x4 kop[D / 16];
-  int rk_slot = 0, rk_mb = 0;  // group-wise keys: the block whose operands read_k loaded
+  int rk_slot = 0, rk_mb = 0;  // group-wise keys: the block whose key rows qk reads
   auto read_k = [&](int slot, int mb, auto k_c) KVQ_INLINE {
     const typename SM::KSlot& ks = sm.k[slot];
     const int krow = 32 * mb + mrow_key(col);
     kbop = sm.prm[slot].kb[32 * mb + col][h];
-    if constexpr (decltype(k_c)::value == kCached) {
-      if constexpr (TG > 0) {
-        rk_slot = slot;
-        rk_mb = mb;
-        if constexpr (NB == 2) kbop2 = sm.prm[slot].kb2[32 * mb + col][h];
-      }
+    if constexpr (decltype(k_c)::value == kCached && TG > 0) {
+      // group-wise keys: qk reads the fp16 key rows one K-step ahead of their MFMAs
+      rk_slot = slot;
+      rk_mb = mb;
+      kop[0] = *reinterpret_cast<const i32x4*>(&ks.kr[krow][HALF * h]);
+    } else if constexpr (decltype(k_c)::value == kCached) {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; kk++) {
-        if constexpr (TG > 0)  // K-step kk: channels 32 kk + 16 h ..
-          kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][32 * kk + 16 * h]);
-        else if constexpr (PERCH)
+        if constexpr (PERCH)
           kop[kk] = *reinterpret_cast<const i32x4*>(&sm.kc(slot)[krow][HALF * h + 16 * kk]);
         else
           kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
       }
-    } else {
+    } else {  // fp16 rows: current-chunk keys (bf16)
 #pragma unroll
       for (int t = 0; t < D / 16; t++) kop[t] = *reinterpret_cast<const i32x4*>(&ks.kr[krow][HALF * h + 8 * t]);
     }
@@ -1085,34 +1096,21 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       const f32x16 zf = {};
       cb[SET] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kbop), qbias, zf, 0, 0, 0);
     }
-    if constexpr (decltype(k_c)::value == kCached && NB == 2) {
-      cb[SET] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kbop2), qbias2, cb[SET], 0, 0, 0);
-    }
     if constexpr (decltype(k_c)::value == kCached && TG > 0) {
-      // one exact int32 sum per channel group, scaled by the key's step of that group
-      const _Float16* dkg = reinterpret_cast<const _Float16*>(&sm.prm[rk_slot].dka[0][0]);
-      f32x16 sf = {};
+      // S = k_hat' . (q'_hi + q'_lo) on fp16 MFMA, fp32 accumulation, K-step by K-step
+      // (each key operand is read one K-step ahead and used by the hi and the lo MFMA)
+      const uint16_t* krow = &sm.k[rk_slot].kr[32 * rk_mb + mrow_key(col)][HALF * h];
+      f32x16 sc = {};
+      i32x4 kcur = kop[0];
 #pragma unroll
-      for (int gq = 0; gq < NG; gq++) {
-        i32x16 a = {};
-#pragma unroll
-        for (int k2 = 0; k2 < KPG; k2++)
-          a = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[gq * KPG + k2], qhi[gq * KPG + k2], a, 0, 0, 0);
-        a = a << 8;
-#pragma unroll
-        for (int k2 = 0; k2 < KPG; k2++)
-          a = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[gq * KPG + k2], qlo[gq * KPG + k2], a, 0, 0, 0);
-#pragma unroll
-        for (int v4 = 0; v4 < 4; v4++) {
-          const f16x4 d4 = *reinterpret_cast<const f16x4*>(&dkg[gq * kBN + 32 * rk_mb + 8 * v4 + 4 * h]);
-#pragma unroll
-          for (int b = 0; b < 4; b++) sf[4 * v4 + b] = fmaf((float)d4[b], (float)a[4 * v4 + b], sf[4 * v4 + b]);
-        }
-        // one group's accumulator at a time: without this fence the groups' MFMA chains
-        // are interleaved and their accumulators spill
-        __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < D / 16; t++) {
+        i32x4 knext = kcur;
+        if (t + 1 < D / 16) knext = *reinterpret_cast<const i32x4*>(krow + 8 * (t + 1));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kcur), q16h[t], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kcur), q16l[t], sc, 0, 0, 0);
+        kcur = knext;
       }
-      sqh[SET] = __builtin_bit_cast(i32x16, sf);
+      sqh[SET] = __builtin_bit_cast(i32x16, sc);
     } else if constexpr (decltype(k_c)::value == kCached) {
       // S = 256 S_hi + S_lo in one accumulator: the hi sums, a shift, then the lo sums
       i32x16 acc_s = {};
@@ -1166,7 +1164,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     constexpr int SET = decltype(set_c)::value;
     if constexpr (decltype(k_c)::value == kCached && TG > 0) {
 #pragma unroll
-      for (int v = 0; v < 16; v++) x[v] = fmaf(a_st, __int_as_float(sqh[SET][v]), cb[SET][v]);
+      for (int v = 0; v < 16; v++) x[v] = fmaf(scale_l2, __int_as_float(sqh[SET][v]), cb[SET][v]);
       if constexpr (EXACT) {
         // the exact correction's terms past the second order, per channel group:
         // -b gains Delta_g^4 (c2 M2^g - Delta_g^2 (c3 M3^g - Delta_g^2 c4 M4^g))
@@ -1351,22 +1349,27 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       }
       // operand reads are issued one phase ahead of their MFMAs (the sched barriers keep
       // the compiler from sinking them): values under the softmax, keys under the PV
+      // (group-wise keys read a block's values after its softmax: their fp16 query halves
+      // take the registers)
+      constexpr bool kLateV = TG > 0 && decltype(k_c)::value == kCached;
       read_k(slot0, 0, k_c);
       qk(set0, k_c);
-      read_v(slot0, 0);
+      if (!kLateV) read_v(slot0, 0);
       __builtin_amdgcn_sched_barrier(0);
       softmax(slot0, 0, set0, k_c, first_c);
+      if (kLateV) read_v(slot0, 0);
       read_k(slot0, 1, k_c);
       __builtin_amdgcn_sched_barrier(0);
       pv();
       qk(set0, k_c);
-      read_v(slot0, 1);
+      if (!kLateV) read_v(slot0, 1);
       __builtin_amdgcn_sched_barrier(0);
       // the key staging (VALU and LDS writes) runs in the shadow of block 1's QK^T MFMAs
       if (stage_k) store_k(U + 2, slot2, k_c);
       if (kEarlyK && T + 3 < n_t) load_k(U + 3, k_c);
       __builtin_amdgcn_sched_barrier(0);
       softmax(slot0, 1, set0, k_c, no);
+      if (kLateV) read_v(slot0, 1);
       pv();
     } else {
       if (stage_k) store_k(U + 2, slot2, k_c);

@@ -44,6 +44,8 @@ OTHERS = {
     "long": ("long", {}, 1),
     "c40_int4": ("c40", {"bits": 4}, 1),
     "c40_q16": ("c40", {"n_q": 16}, 1),
+    "c40_int4_q16": ("c40", {"n_q": 16, "bits": 4}, 1),
+    "long_q16": ("long", {"n_q": 16}, 1),
     "c40_tgroup32": ("c40_tgroup", {"group": 32}, 1),
     "c40_tgroup64": ("c40_tgroup", {"group": 64}, 1),
     "c40_exact": ("c40", {}, 2),

@@ -213,9 +213,9 @@ int jb_attn_mass_batch(const jb_attn_args* calls, int32_t n_calls, void* stream)
 
 /* Few queries (n_q <= 32, per-token keys, correction other than exact): with a workspace of
  * the size jb_attn_workspace_bytes reports, the call streams each head's cached window in
- * one-wave shares (a decode-like regime, bound by the cache stream rather than the matrix
- * cores), computes the current chunk as one more share and merges the shares' partial
- * records; without a workspace (NULL), the main kernel runs unsplit. */
+ * one-wave shares (a decode-like regime: the window is read once per call rather than
+ * once per 256-query block), computes the current chunk as one more share and merges the
+ * shares' partial records; without a workspace (NULL), the main kernel runs unsplit. */
 
 /* Workspace bytes a call with these arguments uses on the current device (0: none).
  * When the grid of query blocks is small for the device (fewer workgroups than its compute

@@ -67,6 +67,10 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+typedef unsigned u32x6 __attribute__((ext_vector_type(6)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -176,6 +180,18 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
 }
 __device__ inline float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// C += A B on the scaled MFMA: A fp4 e2m1 with E8M0 scale 2^1, B fp6 e2m3 with the E8M0
+// scale in byte SEL of sb (per lane, for its 32 elements).
+template <int SEL>
+__device__ inline f32x16 mfma_f4f6(i32x8 a, i32x8 b, f32x16 c, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 2, 0, 128, SEL, (int)sb);
+}
+
+// Element e of a 32-element fp4 / fp6 operand slice (one lane's K half of a 64-channel
+// K-step) is channel kperm6(e) of the 32: the fp4 key nibbles come from the packed codes
+// as (w & 0x33333333, (w >> 2) & 0x33333333) per 16 channels.
+__device__ __host__ constexpr int kperm6(int e) { return 16 * (e >> 4) + 2 * (e & 7) + ((e >> 3) & 1); }
+
 // Map a linear workgroup id to (query block, head) so that all query blocks of a head
 // run on the same XCD (workgroups are dealt to the 8 XCDs round-robin), keeping that
 // head's cache window in one L2.
@@ -274,6 +290,14 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   static_assert(TG == 0 || (!PERCH && TG % 32 == 0 && TG < D && NG <= kNS), "group-wise options");
   constexpr int HALF = D / 2;
   constexpr int KSTEPS = D / 32;  // int8 K-steps of 32 channels
+  // Per-token INT2 keys: QK^T on the scaled fp4 x fp6 MFMA (32x32x64, twice the K of the
+  // int8 MFMA per instruction at its rate): the codes as fp4 e2m1 (value code / 2, block
+  // scale 2), the rotated query as three fp6 e2m3 passes (a rounding, the rounding of its
+  // residual, the rounding of what is left), each with a power-of-two scale per lane and
+  // 32 channels, summed in one fp32 accumulator.
+  constexpr bool kF6 = BITS == 2 && !PERCH && TG == 0;
+  constexpr int KS6 = D / 64;  // fp6 K-steps of 64 channels (a lane holds 32 of each)
+  constexpr int NP6 = 3;       // query passes
   constexpr int CBLK = D / 32;    // 32-channel output blocks
   constexpr int CPW = 32 / BITS;
   constexpr int KW = D * BITS / 32;  // key words per token
@@ -317,6 +341,9 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // group-wise keys: the rotated query as fp16 hi + lo, in the staged key rows' channel order
   f16x8 q16h[TG > 0 ? D / 16 : 1], q16l[TG > 0 ? D / 16 : 1];
   f16x8 qbias;                     // query operand of the bias MFMA
+  i32x8 q6[kF6 ? KS6 : 1][3];      // fp6 query operands: K-step, pass
+  uint32_t q6sc[2] = {0u, 0u};     // their E8M0 scales: passes 0, 1 in byte 2 K-step + pass
+                                   // of the first word, pass 2 in byte K-step of the second
   float m_run = -INFINITY;         // reference max (log2 units); -inf until the first block
   float a_st = 0.f;                // A of this wave's stream
   // Rotated query q' = H q / sqrt(d) (or q) of this lane's half: channels HALF h + i.
@@ -396,8 +423,10 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));  // stream-wide max
     const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
-    const float A = mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
+    const float A = kF6 ? scale_l2 : mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
     int qs = 0;
+    float qs6 = 0.f;  // fp6 path: the sum of the rounded query's channels
+    if constexpr (!kF6) {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; kk++)
 #pragma unroll
@@ -415,6 +444,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         qhi[kk][j] = (int)whi;
         qlo[kk][j] = (int)wlo;
       }
+    }
     qs += __shfl_xor(qs, 32);
     const float G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
     if constexpr (EXACT && TG > 0) {
@@ -456,7 +486,51 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     }
     // query-side factors of the bias MFMA (key side in the tile parameters):
     //   (Delta_j z_j) * w + (Delta_j^2 / 64) * g - m - 65504 * mask_j
-    const float w = -A * (float)qs;
+    if constexpr (kF6) {
+      // The fp6 passes on the hardware conversion (32 floats / 2^ex rounded to e2m3, to
+      // nearest even, saturating at 7.5; element 2j from the first operand's j-th value,
+      // 2j + 1 from the second's) and its inverse. Every pass reads its sources again
+      // after the conversion (the residual), so they cannot share registers with its
+      // result: the conversion writes part of its result before it has read all of them.
+      float qsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < HALF; i++) qsum += qv[i];
+#pragma unroll
+      for (int k6 = 0; k6 < KS6; k6++) {
+        f32x16 s0, s1;  // element 2j: channel 32 k6 + kperm6(2j); 2j + 1: kperm6(2j + 1)
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+          s0[j] = qv[32 * k6 + kperm6(2 * j)];
+          s1[j] = qv[32 * k6 + kperm6(2 * j + 1)];
+        }
+#pragma unroll
+        for (int pass = 0; pass < NP6; pass++) {
+          float mx = 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; j++) mx = fmaxf(mx, fmaxf(fabsf(s0[j]), fabsf(s1[j])));
+          // 2^ex > mx / 7.5 (the fp32 exponent of mx / 7.5, plus one)
+          const int ex = min(max((int)((__float_as_uint(mx * (1.f / 7.5f)) >> 23) & 255u) - 126, -126), 126);
+          const float sc = __uint_as_float((uint32_t)(127 + ex) << 23);
+          const i32x6 c = __builtin_bit_cast(i32x6, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, sc));
+          const f32x32 v = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(u32x6, c), sc);
+#pragma unroll
+          for (int j = 0; j < 16; j++) {
+            s0[j] -= v[2 * j];
+            s1[j] -= v[2 * j + 1];
+          }
+          q6[k6][pass] = i32x8{c[0], c[1], c[2], c[3], c[4], c[5], 0, 0};
+          if (pass < 2)
+            q6sc[0] |= (uint32_t)(ex + 127) << (8 * (2 * k6 + pass));
+          else
+            q6sc[1] |= (uint32_t)(ex + 127) << (8 * k6);
+        }
+        // sum of the rounded channels = sum of q' minus what the passes left
+#pragma unroll
+        for (int j = 0; j < 16; j++) qsum -= s0[j] + s1[j];
+      }
+      qs6 = qsum + xor32(qsum);
+    }
+    const float w = -A * (kF6 ? qs6 : (float)qs);
     const float g = -G * kD2Scale;
     _Float16 wh, wl, gh, gl;
     split16(w, wh, wl);
@@ -824,6 +898,10 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           dst[1] = make_uint4(res[4], res[5], res[6], res[7]);
         } else if constexpr (PERCH) {  // packed code slots
           *reinterpret_cast<uint4*>(&sm.kc(slot)[tok][16 * ui]) = lo;
+        } else if constexpr (kF6) {
+          // fp4 nibbles of channels 16 ui + 2 n (first word) and 16 ui + 2 n + 1 (second)
+          const uint32_t w = kpre[i].x;
+          *reinterpret_cast<uint2*>(&ks.c[tok][8 * ui]) = make_uint2(w & 0x33333333u, (w >> 2) & 0x33333333u);
         } else {
           *reinterpret_cast<uint4*>(&ks.c[tok][16 * ui]) = lo;
         }
@@ -1066,6 +1144,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // bf16 key rows (current), read from LDS ahead of their MFMAs.
   uint4 kbop;
   i32x4 kop[D / 16];
+  i32x8 kop6[kF6 ? KS6 : 1];  // fp4 key operands (4 of 8 words used)
   int rk_slot = 0, rk_mb = 0;  // group-wise keys: the block whose key rows qk reads
   auto read_k = [&](int slot, int mb, auto k_c) KVQ_INLINE {
     const typename SM::KSlot& ks = sm.k[slot];
@@ -1081,8 +1160,16 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       for (int kk = 0; kk < KSTEPS; kk++) {
         if constexpr (PERCH)
           kop[kk] = *reinterpret_cast<const i32x4*>(&sm.kc(slot)[krow][HALF * h + 16 * kk]);
-        else
+        else if constexpr (!kF6)
           kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
+      }
+      if constexpr (kF6) {
+        // fp4 rows: channel c at nibble c of the row (in kperm6 order per 32 channels)
+#pragma unroll
+        for (int k6 = 0; k6 < KS6; k6++) {
+          const uint4 w4 = *reinterpret_cast<const uint4*>(&ks.c[krow][(HALF * h + 32 * k6) / 2]);
+          kop6[k6] = i32x8{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w, 0, 0, 0, 0};
+        }
       }
     } else {  // fp16 rows: current-chunk keys (bf16)
 #pragma unroll
@@ -1110,6 +1197,17 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kcur), q16l[t], sc, 0, 0, 0);
         kcur = knext;
       }
+      sqh[SET] = __builtin_bit_cast(i32x16, sc);
+    } else if constexpr (decltype(k_c)::value == kCached && kF6) {
+      // S = sum_c q'_c code_c in fp32, pass by pass; the key scale 2^1 (E8M0 128) turns the
+      // fp4 values code / 2 into the codes
+      f32x16 sc = {};
+      sc = mfma_f4f6<0>(kop6[0], q6[0][0], sc, q6sc[0]);
+      if constexpr (KS6 > 1) sc = mfma_f4f6<2>(kop6[1], q6[1][0], sc, q6sc[0]);
+      sc = mfma_f4f6<1>(kop6[0], q6[0][1], sc, q6sc[0]);
+      if constexpr (KS6 > 1) sc = mfma_f4f6<3>(kop6[1], q6[1][1], sc, q6sc[0]);
+      sc = mfma_f4f6<0>(kop6[0], q6[0][2], sc, q6sc[1]);
+      if constexpr (KS6 > 1) sc = mfma_f4f6<1>(kop6[1], q6[1][2], sc, q6sc[1]);
       sqh[SET] = __builtin_bit_cast(i32x16, sc);
     } else if constexpr (decltype(k_c)::value == kCached) {
       // S = 256 S_hi + S_lo in one accumulator: the hi sums, a shift, then the lo sums
@@ -1194,7 +1292,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
 #pragma unroll
         for (int b = 0; b < 4; b++) {
           const int v = 4 * v4 + b;
-          x[v] = fmaf(d[b], (float)sqh[SET][v], cb[SET][v]);
+          x[v] = fmaf(d[b], kF6 ? __int_as_float(sqh[SET][v]) : (float)sqh[SET][v], cb[SET][v]);
         }
         if constexpr (EXACT && !PERCH) {
           // the exact correction's terms past the second order: -b gains

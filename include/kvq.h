@@ -174,8 +174,11 @@ typedef struct {
 } jb_attn_args;
 
 /* Corrected attention forward: writes o and, if given, mass_s/mass_r.
- * Numerics: cached-key scores use the rotated query as a 16-bit fixed-point integer
- * (one scale per 32 queries) against the exact integer codes; softmax numerators are
+ * Numerics: with 2-bit per-token keys, cached-key scores take the rotated query as the
+ * sum of three fp6 (e2m3) roundings (the query, then twice what is left), each with a
+ * power-of-two scale per query and 32 channels, against the exact codes, summed in
+ * fp32; with 4-bit or per-channel keys, the rotated query as a 16-bit fixed-point
+ * integer (one scale per 32 queries) against the exact codes; softmax numerators are
  * fp16 (relative to a per-query reference max that is raised whenever a numerator could
  * leave the fp16 range), values fp16((code - z) Delta); sums and outputs fp32.
  * Preconditions on the data (not checked): key steps Delta < 2048 and |Delta z| < 65504

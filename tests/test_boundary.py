@@ -202,3 +202,18 @@ def test_window_ring_bookkeeping(kvq):
     bf16 = 2 * 40 * 8 * 4680 * 128 * 2
     assert w2 == 2 * 40 * 8 * 4736 * (32 + 4)      # padded tokens: 32 code bytes + fp16 step and zero
     assert abs(w2 / w4 - 0.529) < 1e-3 and w2 / bf16 < 0.15
+
+
+def test_build_refuses_conversions_over_their_sources():
+    # the build's check of the device assembly (MX conversions whose result overlaps a
+    # source register read the overwritten values; the build refuses such code)
+    from bit_kv_cache_kvq_amd.build import overlapping_conversions
+    asm = "\n".join([
+        "\tv_cvt_scalef32_2xpk16_fp6_f32 v[32:37], v[2:17], v[18:33], s0",   # overlaps v32, v33
+        "\tv_cvt_scalef32_2xpk16_fp6_f32 v[34:39], v[2:17], v[18:33], v41",
+        "\tv_cvt_scalef32_pk32_f32_fp6 v[0:31], v[32:37], s0 ; comment v[0:40]",
+        "\tv_cvt_scalef32_pk32_f32_fp6 v[0:31], v[30:35], v36",              # overlaps v30, v31
+        "\tv_mov_b32 v1, v1",
+    ])
+    assert overlapping_conversions(asm) == ["v_cvt_scalef32_2xpk16_fp6_f32 v[32:37], v[2:17], v[18:33], s0",
+                                            "v_cvt_scalef32_pk32_f32_fp6 v[0:31], v[30:35], v36"]

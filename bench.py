@@ -27,6 +27,20 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
+PEAK_FP6_TFLOPS = 10100.0        # MI355X dense fp6/fp4 MFMA
+FP6_PASSES = 3                   # query passes of the fp4 x fp6 QK^T
+
+
+def fp6_qk(w, decode):
+    """Whether the attention kernel runs QK^T on the scaled fp4 x fp6 MFMA: 2-bit
+    per-token keys in the main kernel (not the few-query path, not group-wise keys)."""
+    return w.bits == 2 and w.k_granularity == "token" and not decode
+
+
+def mixed_peak():
+    """The peak of the fp6 path's instruction mix: half the algorithmic FLOPs (QK^T) run as
+    FP6_PASSES fp6 passes at the fp6 peak, the other half (PV) at the fp16 peak."""
+    return 1.0 / (0.5 * FP6_PASSES / PEAK_FP6_TFLOPS + 0.5 / PEAK_MFMA_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 METRIC = "jb_attn TFLOP/s + cache GB/s (% roofline), INT2 corrected, 40H d128 chunk 4680"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "jb_attn_c40_counters.md")
@@ -190,6 +204,8 @@ def measure_other(key, launches=OTHER_LAUNCHES, warmup=3):
         rec.update({"bound": "hbm", "GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)})
     else:
         rec.update({"bound": "mfma", "frac": round(w.flops() / (med * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)})
+        if fp6_qk(w, decode):
+            rec["frac_mixed"] = round(w.flops() / (med * 1e-3) / 1e12 / mixed_peak(), 4)
     del ws, q, kr, vr, kwin, vwin, o, ms, mr
     torch.cuda.empty_cache()
     return rec
@@ -344,7 +360,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8+fp16",
+        "dtype": ("fp4xfp6+fp16" if fp6_qk(w, decode) else
+                  "fp16" if w.k_granularity == "token_group" else "int8+fp16"),
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} d={w.d}, current chunk {w.n_q} tokens, window "
                                f"{w.n_chunks}x{w.chunk_len} cached tokens, INT{w.bits} {gran_text(w, w.k_granularity)} K, "
@@ -365,6 +382,8 @@ def main():
                       "frac": round(achieved / PEAK_MFMA_TFLOPS, 4)} if not decode else
                      {"bound": "hbm", "achieved": round(algo_bytes / (attn_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(algo_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+        | ({"peak_mixed": round(mixed_peak(), 1), "frac_mixed": round(achieved / mixed_peak(), 4)}
+           if fp6_qk(w, decode) else {})
         | {"traffic": (round(traffic) if traffic is not None else None),
            "algorithmic_bytes": algo_bytes, "kernel_source_sha256_16": kernel_source_hash(),
            "mfma_busy": ctr.get("mfma_busy"), "valu_busy": ctr.get("valu_busy")},

@@ -270,6 +270,85 @@ struct Smem<D, true, 0> : SmemSlots<D> {
 
 #define KVQ_INLINE __attribute__((always_inline))
 
+// The rotated query of one lane (qv[i]: channel HALF h + i of its query) as three fp6
+// e2m3 roundings per 64-channel K-step, for the scaled fp4 x fp6 QK^T: K-step k6 holds
+// channels 32 k6 + kperm6(e), e < 32; pass 0 rounds them with a power-of-two scale
+// 2^ex > max|.| / 7.5, passes 1 and 2 round what is left the same way. Writes the
+// operands q6[k6][pass] and their E8M0 scale bytes (passes 0 and 1 of K-step k6 in bytes
+// 2 k6 and 2 k6 + 1 of sc[0], pass 2 in byte k6 of sc[1]); returns the lane's sum of the
+// rounded channels.
+// The rounding is the hardware conversion (32 floats / scale to packed e2m3, to nearest
+// even, saturating at 7.5; packed element 2j from the first operand's j-th value, 2j + 1
+// from the second's) and its inverse gives the rounded values. Every pass reads its
+// sources again after the conversion (the residual), which keeps them out of the
+// conversion's result registers: it writes part of its result before it has read all
+// of its sources.
+template <int HALF>
+__device__ KVQ_INLINE float encode_query_fp6(const float (&qv)[HALF], i32x8 (&q6)[HALF / 32][3], uint32_t (&sc)[2]) {
+  float qsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < HALF; i++) qsum += qv[i];
+  sc[0] = 0u;
+  sc[1] = 0u;
+#pragma unroll
+  for (int k6 = 0; k6 < HALF / 32; k6++) {
+    f32x16 s0, s1;  // element 2j: channel 32 k6 + kperm6(2j); 2j + 1: kperm6(2j + 1)
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      s0[j] = qv[32 * k6 + kperm6(2 * j)];
+      s1[j] = qv[32 * k6 + kperm6(2 * j + 1)];
+    }
+#pragma unroll
+    for (int pass = 0; pass < 3; pass++) {
+      float mx = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; j++) mx = fmaxf(mx, fmaxf(fabsf(s0[j]), fabsf(s1[j])));
+      // 2^ex > mx / 7.5 (the fp32 exponent of mx / 7.5, plus one)
+      const int ex = min(max((int)((__float_as_uint(mx * (1.f / 7.5f)) >> 23) & 255u) - 126, -126), 126);
+      const float scl = __uint_as_float((uint32_t)(127 + ex) << 23);
+      const i32x6 c = __builtin_bit_cast(i32x6, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, scl));
+      const f32x32 v = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(u32x6, c), scl);
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        s0[j] -= v[2 * j];
+        s1[j] -= v[2 * j + 1];
+      }
+      q6[k6][pass] = i32x8{c[0], c[1], c[2], c[3], c[4], c[5], 0, 0};
+      if (pass < 2)
+        sc[0] |= (uint32_t)(ex + 127) << (8 * (2 * k6 + pass));
+      else
+        sc[1] |= (uint32_t)(ex + 127) << (8 * k6);
+    }
+    // the sum of the rounded channels: the sum of q' minus what the passes left
+#pragma unroll
+    for (int j = 0; j < 16; j++) qsum -= s0[j] + s1[j];
+  }
+  return qsum;
+}
+
+// S = sum_c q~_c code_c of one 32x32 block in fp32: six scaled MFMAs (three query passes
+// x two 64-channel K-steps; D = 64: three), the fp4 key operands ka (code c as the e2m1
+// value c / 2, key scale 2^1 = E8M0 128) against encode_query_fp6's operands.
+template <int KS6>  // deduced from the operand arrays
+__device__ KVQ_INLINE f32x16 qk_fp6(const i32x8 (&ka)[KS6], const i32x8 (&q6)[KS6][3], const uint32_t (&sc)[2]) {
+  f32x16 acc = {};
+  acc = mfma_f4f6<0>(ka[0], q6[0][0], acc, sc[0]);
+  if constexpr (KS6 > 1) acc = mfma_f4f6<2>(ka[1], q6[1][0], acc, sc[0]);
+  acc = mfma_f4f6<1>(ka[0], q6[0][1], acc, sc[0]);
+  if constexpr (KS6 > 1) acc = mfma_f4f6<3>(ka[1], q6[1][1], acc, sc[0]);
+  acc = mfma_f4f6<0>(ka[0], q6[0][2], acc, sc[1]);
+  if constexpr (KS6 > 1) acc = mfma_f4f6<1>(ka[1], q6[1][2], acc, sc[1]);
+  return acc;
+}
+
+// fp4 key operand of 32 channels from two packed INT2 words (16 channels each, channel
+// k at bits 2k): nibble n of the four dwords is channel 2n, 2n + 1 of the first word, then
+// of the second (the kperm6 order).
+__device__ inline i32x8 fp4_key_operand(uint32_t w0, uint32_t w1) {
+  return i32x8{(int)(w0 & 0x33333333u), (int)((w0 >> 2) & 0x33333333u), (int)(w1 & 0x33333333u),
+               (int)((w1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+}
+
 enum : int { kNone = 0, kCached = 1, kCurrent = 2 };
 template <int K>
 using Kind = std::integral_constant<int, K>;
@@ -297,7 +376,6 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // 32 channels, summed in one fp32 accumulator.
   constexpr bool kF6 = BITS == 2 && !PERCH && TG == 0;
   constexpr int KS6 = D / 64;  // fp6 K-steps of 64 channels (a lane holds 32 of each)
-  constexpr int NP6 = 3;       // query passes
   constexpr int CBLK = D / 32;    // 32-channel output blocks
   constexpr int CPW = 32 / BITS;
   constexpr int KW = D * BITS / 32;  // key words per token
@@ -342,8 +420,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   f16x8 q16h[TG > 0 ? D / 16 : 1], q16l[TG > 0 ? D / 16 : 1];
   f16x8 qbias;                     // query operand of the bias MFMA
   i32x8 q6[kF6 ? KS6 : 1][3];      // fp6 query operands: K-step, pass
-  uint32_t q6sc[2] = {0u, 0u};     // their E8M0 scales: passes 0, 1 in byte 2 K-step + pass
-                                   // of the first word, pass 2 in byte K-step of the second
+  uint32_t q6sc[2] = {0u, 0u};     // their E8M0 scale bytes
   float m_run = -INFINITY;         // reference max (log2 units); -inf until the first block
   float a_st = 0.f;                // A of this wave's stream
   // Rotated query q' = H q / sqrt(d) (or q) of this lane's half: channels HALF h + i.
@@ -487,48 +564,8 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     // query-side factors of the bias MFMA (key side in the tile parameters):
     //   (Delta_j z_j) * w + (Delta_j^2 / 64) * g - m - 65504 * mask_j
     if constexpr (kF6) {
-      // The fp6 passes on the hardware conversion (32 floats / 2^ex rounded to e2m3, to
-      // nearest even, saturating at 7.5; element 2j from the first operand's j-th value,
-      // 2j + 1 from the second's) and its inverse. Every pass reads its sources again
-      // after the conversion (the residual), so they cannot share registers with its
-      // result: the conversion writes part of its result before it has read all of them.
-      float qsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < HALF; i++) qsum += qv[i];
-#pragma unroll
-      for (int k6 = 0; k6 < KS6; k6++) {
-        f32x16 s0, s1;  // element 2j: channel 32 k6 + kperm6(2j); 2j + 1: kperm6(2j + 1)
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-          s0[j] = qv[32 * k6 + kperm6(2 * j)];
-          s1[j] = qv[32 * k6 + kperm6(2 * j + 1)];
-        }
-#pragma unroll
-        for (int pass = 0; pass < NP6; pass++) {
-          float mx = 0.f;
-#pragma unroll
-          for (int j = 0; j < 16; j++) mx = fmaxf(mx, fmaxf(fabsf(s0[j]), fabsf(s1[j])));
-          // 2^ex > mx / 7.5 (the fp32 exponent of mx / 7.5, plus one)
-          const int ex = min(max((int)((__float_as_uint(mx * (1.f / 7.5f)) >> 23) & 255u) - 126, -126), 126);
-          const float sc = __uint_as_float((uint32_t)(127 + ex) << 23);
-          const i32x6 c = __builtin_bit_cast(i32x6, __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, sc));
-          const f32x32 v = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(__builtin_bit_cast(u32x6, c), sc);
-#pragma unroll
-          for (int j = 0; j < 16; j++) {
-            s0[j] -= v[2 * j];
-            s1[j] -= v[2 * j + 1];
-          }
-          q6[k6][pass] = i32x8{c[0], c[1], c[2], c[3], c[4], c[5], 0, 0};
-          if (pass < 2)
-            q6sc[0] |= (uint32_t)(ex + 127) << (8 * (2 * k6 + pass));
-          else
-            q6sc[1] |= (uint32_t)(ex + 127) << (8 * k6);
-        }
-        // sum of the rounded channels = sum of q' minus what the passes left
-#pragma unroll
-        for (int j = 0; j < 16; j++) qsum -= s0[j] + s1[j];
-      }
-      qs6 = qsum + xor32(qsum);
+      const float lsum = encode_query_fp6<HALF>(qv, q6, q6sc);
+      qs6 = lsum + xor32(lsum);
     }
     const float w = -A * (kF6 ? qs6 : (float)qs);
     const float g = -G * kD2Scale;
@@ -1201,14 +1238,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     } else if constexpr (decltype(k_c)::value == kCached && kF6) {
       // S = sum_c q'_c code_c in fp32, pass by pass; the key scale 2^1 (E8M0 128) turns the
       // fp4 values code / 2 into the codes
-      f32x16 sc = {};
-      sc = mfma_f4f6<0>(kop6[0], q6[0][0], sc, q6sc[0]);
-      if constexpr (KS6 > 1) sc = mfma_f4f6<2>(kop6[1], q6[1][0], sc, q6sc[0]);
-      sc = mfma_f4f6<1>(kop6[0], q6[0][1], sc, q6sc[0]);
-      if constexpr (KS6 > 1) sc = mfma_f4f6<3>(kop6[1], q6[1][1], sc, q6sc[0]);
-      sc = mfma_f4f6<0>(kop6[0], q6[0][2], sc, q6sc[1]);
-      if constexpr (KS6 > 1) sc = mfma_f4f6<1>(kop6[1], q6[1][2], sc, q6sc[1]);
-      sqh[SET] = __builtin_bit_cast(i32x16, sc);
+      sqh[SET] = __builtin_bit_cast(i32x16, qk_fp6(kop6, q6, q6sc));
     } else if constexpr (decltype(k_c)::value == kCached) {
       // S = 256 S_hi + S_lo in one accumulator: the hi sums, a shift, then the lo sums
       i32x16 acc_s = {};
@@ -1794,8 +1824,13 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
   const int qi = q_ok ? col : 0;
   const float scale_l2 = p.s * kLog2e;
 
-  // ---- query operands: rotated query as 16-bit fixed point, int8 hi/lo (main kernel's build)
-  i32x4 qhi[KSTEPS], qlo[KSTEPS];
+  // ---- query operands: 2-bit keys, the rotated query as three fp6 passes (scaled fp4 x fp6
+  // QK^T); 4-bit keys, as 16-bit fixed point split into int8 hi/lo (the main kernel's builds)
+  constexpr bool kF6 = BITS == 2;
+  constexpr int KS6 = D / 64;
+  i32x4 qhi[kF6 ? 1 : KSTEPS], qlo[kF6 ? 1 : KSTEPS];
+  i32x8 q6[kF6 ? KS6 : 1][3];
+  uint32_t q6sc[2] = {0u, 0u};
   f16x8 qbias;
   float A;
   {
@@ -1843,30 +1878,38 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
     ss += xor32(ss);
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));
-    const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
-    A = mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
-    int qs = 0;
+    float qsum;  // the sum of the query channels as the QK^T operands hold them
+    if constexpr (kF6) {
+      A = scale_l2;
+      const float lsum = encode_query_fp6<HALF>(qv, q6, q6sc);
+      qsum = lsum + xor32(lsum);
+    } else {
+      const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
+      A = mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
+      int qs = 0;
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; kk++)
+      for (int kk = 0; kk < KSTEPS; kk++)
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        uint32_t whi = 0, wlo = 0;
+        for (int j = 0; j < 4; j++) {
+          uint32_t whi = 0, wlo = 0;
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-          const int qf = (int)__builtin_rintf(qv[16 * kk + kperm<BITS>(j, b)] * inv);
-          const int hi = (qf + 128) >> 8;
-          const int lo = qf - (hi << 8);
-          qs += qf;
-          whi |= (uint32_t)(hi & 0xFF) << (8 * b);
-          wlo |= (uint32_t)(lo & 0xFF) << (8 * b);
+          for (int b = 0; b < 4; b++) {
+            const int qf = (int)__builtin_rintf(qv[16 * kk + kperm<BITS>(j, b)] * inv);
+            const int hi = (qf + 128) >> 8;
+            const int lo = qf - (hi << 8);
+            qs += qf;
+            whi |= (uint32_t)(hi & 0xFF) << (8 * b);
+            wlo |= (uint32_t)(lo & 0xFF) << (8 * b);
+          }
+          qhi[kk][j] = (int)whi;
+          qlo[kk][j] = (int)wlo;
         }
-        qhi[kk][j] = (int)whi;
-        qlo[kk][j] = (int)wlo;
-      }
-    qs += __shfl_xor(qs, 32);
+      qs += __shfl_xor(qs, 32);
+      qsum = (float)qs;
+    }
     const float G = p.correction ? p.s * p.s * ss * (1.f / 24.f) * kLog2e : 0.f;
     _Float16 wh, wl, gh, gl;
-    split16(-A * (float)qs, wh, wl);
+    split16(-A * qsum, wh, wl);
     split16(-G * kD2Scale, gh, gl);
     if (h == 0) {
       qbias[0] = wh;
@@ -1983,28 +2026,34 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
         const uint32_t one = 0x3C00u;
         kbop = make_uint4(one | (one << 16), kv ? 0u : one, 0u, 0u);
       }
-      // key codes as int8 (kperm order in each 16-channel unit)
-      i32x4 kop[KSTEPS];
+      const f32x16 zf = {};
+      const f32x16 cbv = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kbop), qbias, zf, 0, 0, 0);
+      float sqf[16];  // S = sum_c q_c code_c of this lane's 16 scores
+      if constexpr (kF6) {
+        i32x8 ka[KS6];
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk++) {
-        if constexpr (BITS == 2) {
-          const uint32_t w = cur.k[mb][kk];
-          kop[kk] = i32x4{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u), (int)((w >> 4) & 0x03030303u),
-                          (int)((w >> 6) & 0x03030303u)};
-        } else {
+        for (int k6 = 0; k6 < KS6; k6++) ka[k6] = fp4_key_operand(cur.k[mb][2 * k6], cur.k[mb][2 * k6 + 1]);
+        const f32x16 sf = qk_fp6(ka, q6, q6sc);
+#pragma unroll
+        for (int v = 0; v < 16; v++) sqf[v] = sf[v];
+      } else {
+        // key codes as int8 (kperm order in each 16-channel unit)
+        i32x4 kop[KSTEPS];
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; kk++) {
           const uint32_t w0 = cur.k[mb][2 * kk], w1 = cur.k[mb][2 * kk + 1];
           kop[kk] = i32x4{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
                           (int)((w1 >> 4) & 0x0F0F0F0Fu)};
         }
+        i32x16 sq = {};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; kk++) sq = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[kk], qhi[kk], sq, 0, 0, 0);
+        sq = sq << 8;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; kk++) sq = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[kk], qlo[kk], sq, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; v++) sqf[v] = (float)sq[v];
       }
-      const f32x16 zf = {};
-      const f32x16 cbv = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kbop), qbias, zf, 0, 0, 0);
-      i32x16 sq = {};
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk++) sq = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[kk], qhi[kk], sq, 0, 0, 0);
-      sq = sq << 8;
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk++) sq = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[kk], qlo[kk], sq, 0, 0, 0);
       // logits (log2 units, -m through the bias) and softmax numerators
       float x[16];
 #pragma unroll
@@ -2012,7 +2061,7 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
         const float4 d4 = *reinterpret_cast<const float4*>(&sm.dka[32 * mb + 8 * v4 + 4 * h]);
         const float d[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int b = 0; b < 4; b++) x[4 * v4 + b] = fmaf(d[b], (float)sq[4 * v4 + b], cbv[4 * v4 + b]);
+        for (int b = 0; b < 4; b++) x[4 * v4 + b] = fmaf(d[b], sqf[4 * v4 + b], cbv[4 * v4 + b]);
       }
       auto pairs = [&](float off) KVQ_INLINE {
         float ls2[2] = {0.f, 0.f};

@@ -183,6 +183,9 @@ def make_args(q, k_cur, v_cur, k_window, v_window, chunk_len, n_chunks, k_fmt, v
     """Fill a JbAttnArgs from tensors. k_window / v_window are (codes, scale, zero) or None;
     window_chunks is their per-head chunk capacity when it exceeds n_chunks (0: n_chunks).
 
+    The struct holds raw device pointers; it also keeps references to the tensors, so that
+    tensors made inline in the call are not freed (and their memory handed to the next
+    allocation, such as the workspace) while the struct is in use.
     The workspace is left empty (the call then runs unsplit); attach_workspace adds it."""
     B, H, n_q, d = q.shape
     n_r = k_cur.shape[2] if k_cur is not None else 0
@@ -190,10 +193,12 @@ def make_args(q, k_cur, v_cur, k_window, v_window, chunk_len, n_chunks, k_fmt, v
     vw = v_window if v_window is not None else (None, None, None)
     for t in (q, k_cur, v_cur, o, mass_s, mass_r, *kw, *vw):
         assert t is None or t.is_contiguous()
-    return JbAttnArgs(B, H, d, n_q, n_r, chunk_len, n_chunks, _ptr(q), _ptr(k_cur), _ptr(v_cur),
+    args = JbAttnArgs(B, H, d, n_q, n_r, chunk_len, n_chunks, _ptr(q), _ptr(k_cur), _ptr(v_cur),
                       _ptr(kw[0]), _ptr(kw[1]), _ptr(kw[2]), _ptr(vw[0]), _ptr(vw[1]), _ptr(vw[2]),
                       k_fmt, v_fmt, float(softmax_scale), int(correction), _ptr(o), _ptr(mass_s), _ptr(mass_r),
                       None, 0, int(window_chunks))
+    args.tensors = tuple(t for t in (q, k_cur, v_cur, *kw, *vw, o, mass_s, mass_r) if t is not None)
+    return args
 
 
 def jb_attn_fwd(args: JbAttnArgs, stream=None):
@@ -237,14 +242,16 @@ def jb_attn_workspace_bytes(args: JbAttnArgs) -> int:
 
 def attach_workspace(args: JbAttnArgs, device="cuda"):
     """Allocate the split-window workspace the library asks for on the current device and
-    point args at it. Returns the tensor (None when no split is planned); it must stay
-    alive while calls made with args are in flight."""
+    point args at it. Returns the tensor (None when no split is planned); args also keeps a
+    reference to it, like to its other tensors."""
     n = jb_attn_workspace_bytes(args)
     if n == 0:
         args.workspace, args.workspace_bytes = None, 0
+        args.workspace_tensor = None
         return None
     ws = torch.empty(n, dtype=torch.uint8, device=device)
     args.workspace, args.workspace_bytes = ctypes.c_void_p(ws.data_ptr()), n
+    args.workspace_tensor = ws
     return ws
 
 

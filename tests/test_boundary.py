@@ -217,3 +217,30 @@ def test_build_refuses_conversions_over_their_sources():
     ])
     assert overlapping_conversions(asm) == ["v_cvt_scalef32_2xpk16_fp6_f32 v[32:37], v[2:17], v[18:33], s0",
                                             "v_cvt_scalef32_pk32_f32_fp6 v[0:31], v[30:35], v36"]
+
+
+def test_args_keep_their_tensors_alive(kvq):
+    # the struct holds raw pointers: tensors made inline in make_args must live as long as
+    # the struct (else their memory goes to the next allocation, e.g. the workspace)
+    import gc
+    import weakref
+
+    import torch
+    fmt = kvq.KvqFormat.make(2, "token", 128, True, "key")
+    vfmt = kvq.KvqFormat.make(2, "token", 128, True, "value")
+    refs = []
+
+    def t(*shape, dtype=torch.int16):
+        x = torch.zeros(*shape, dtype=dtype)
+        refs.append(weakref.ref(x))
+        return x
+
+    a = kvq.make_args(t(1, 1, 64, 128), t(1, 1, 64, 128), t(1, 1, 64, 128), (t(1, 1, 64, 8, dtype=torch.int32),
+                      t(1, 1, 64), t(1, 1, 64)), (t(1, 1, 64, 8, dtype=torch.int32), t(1, 1, 64), t(1, 1, 64)),
+                      64, 1, fmt, vfmt, o=t(1, 1, 64, 128, dtype=torch.float32))
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    assert a.q == a.tensors[0].data_ptr()
+    del a
+    gc.collect()
+    assert all(r() is None for r in refs)

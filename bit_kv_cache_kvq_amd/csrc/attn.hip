@@ -180,17 +180,21 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
 }
 __device__ inline float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// C += A B on the scaled MFMA: A fp4 e2m1 with E8M0 scale 2^1, B fp6 e2m3 with the E8M0
-// scale in byte SEL of sb (per lane, for its 32 elements).
-template <int SEL>
-__device__ inline f32x16 mfma_f4f6(i32x8 a, i32x8 b, f32x16 c, uint32_t sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 2, 0, 128, SEL, (int)sb);
+// C += A B on the scaled MFMA: A (keys) fp4 e2m1 (FA = 4) or fp6 e2m3 (FA = 2) with E8M0
+// scale 2^1, B fp6 e2m3 with the E8M0 scale in byte SEL of sb (per lane, for its 32
+// elements).
+template <int FA, int SEL>
+__device__ inline f32x16 mfma_kq(i32x8 a, i32x8 b, f32x16 c, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, 2, 0, 128, SEL, (int)sb);
 }
 
-// Element e of a 32-element fp4 / fp6 operand slice (one lane's K half of a 64-channel
-// K-step) is channel kperm6(e) of the 32: the fp4 key nibbles come from the packed codes
-// as (w & 0x33333333, (w >> 2) & 0x33333333) per 16 channels.
+// Element e of a 32-element operand slice (one lane's K half of a 64-channel K-step) is
+// channel kslot<BITS>(e) of the 32: 2-bit keys, the fp4 nibbles come from the packed codes
+// as (w & 0x33333333, (w >> 2) & 0x33333333) per 16 channels; 4-bit keys are converted
+// to fp6 in channel order.
 __device__ __host__ constexpr int kperm6(int e) { return 16 * (e >> 4) + 2 * (e & 7) + ((e >> 3) & 1); }
+template <int BITS>
+__device__ __host__ constexpr int kslot(int e) { return BITS == 2 ? kperm6(e) : e; }
 
 // Map a linear workgroup id to (query block, head) so that all query blocks of a head
 // run on the same XCD (workgroups are dealt to the 8 XCDs round-robin), keeping that
@@ -271,8 +275,8 @@ struct Smem<D, true, 0> : SmemSlots<D> {
 #define KVQ_INLINE __attribute__((always_inline))
 
 // The rotated query of one lane (qv[i]: channel HALF h + i of its query) as three fp6
-// e2m3 roundings per 64-channel K-step, for the scaled fp4 x fp6 QK^T: K-step k6 holds
-// channels 32 k6 + kperm6(e), e < 32; pass 0 rounds them with a power-of-two scale
+// e2m3 roundings per 64-channel K-step, for the scaled-MFMA QK^T: K-step k6 holds
+// channels 32 k6 + kslot<BITS>(e), e < 32; pass 0 rounds them with a power-of-two scale
 // 2^ex > max|.| / 7.5, passes 1 and 2 round what is left the same way. Writes the
 // operands q6[k6][pass] and their E8M0 scale bytes (passes 0 and 1 of K-step k6 in bytes
 // 2 k6 and 2 k6 + 1 of sc[0], pass 2 in byte k6 of sc[1]); returns the lane's sum of the
@@ -283,7 +287,7 @@ struct Smem<D, true, 0> : SmemSlots<D> {
 // sources again after the conversion (the residual), which keeps them out of the
 // conversion's result registers: it writes part of its result before it has read all
 // of its sources.
-template <int HALF>
+template <int HALF, int BITS>
 __device__ KVQ_INLINE float encode_query_fp6(const float (&qv)[HALF], i32x8 (&q6)[HALF / 32][3], uint32_t (&sc)[2]) {
   float qsum = 0.f;
 #pragma unroll
@@ -292,11 +296,11 @@ __device__ KVQ_INLINE float encode_query_fp6(const float (&qv)[HALF], i32x8 (&q6
   sc[1] = 0u;
 #pragma unroll
   for (int k6 = 0; k6 < HALF / 32; k6++) {
-    f32x16 s0, s1;  // element 2j: channel 32 k6 + kperm6(2j); 2j + 1: kperm6(2j + 1)
+    f32x16 s0, s1;  // element 2j: channel 32 k6 + kslot(2j); 2j + 1: kslot(2j + 1)
 #pragma unroll
     for (int j = 0; j < 16; j++) {
-      s0[j] = qv[32 * k6 + kperm6(2 * j)];
-      s1[j] = qv[32 * k6 + kperm6(2 * j + 1)];
+      s0[j] = qv[32 * k6 + kslot<BITS>(2 * j)];
+      s1[j] = qv[32 * k6 + kslot<BITS>(2 * j + 1)];
     }
 #pragma unroll
     for (int pass = 0; pass < 3; pass++) {
@@ -327,18 +331,40 @@ __device__ KVQ_INLINE float encode_query_fp6(const float (&qv)[HALF], i32x8 (&q6
 }
 
 // S = sum_c q~_c code_c of one 32x32 block in fp32: six scaled MFMAs (three query passes
-// x two 64-channel K-steps; D = 64: three), the fp4 key operands ka (code c as the e2m1
-// value c / 2, key scale 2^1 = E8M0 128) against encode_query_fp6's operands.
-template <int KS6>  // deduced from the operand arrays
+// x two 64-channel K-steps; D = 64: three), the key operands ka (code c as the value
+// c / 2: fp4 e2m1 for 2-bit codes, FA = 4, fp6 e2m3 for 4-bit codes, FA = 2; key scale
+// 2^1 = E8M0 128) against encode_query_fp6's operands.
+template <int FA, int KS6>  // KS6 deduced from the operand arrays
 __device__ KVQ_INLINE f32x16 qk_fp6(const i32x8 (&ka)[KS6], const i32x8 (&q6)[KS6][3], const uint32_t (&sc)[2]) {
   f32x16 acc = {};
-  acc = mfma_f4f6<0>(ka[0], q6[0][0], acc, sc[0]);
-  if constexpr (KS6 > 1) acc = mfma_f4f6<2>(ka[1], q6[1][0], acc, sc[0]);
-  acc = mfma_f4f6<1>(ka[0], q6[0][1], acc, sc[0]);
-  if constexpr (KS6 > 1) acc = mfma_f4f6<3>(ka[1], q6[1][1], acc, sc[0]);
-  acc = mfma_f4f6<0>(ka[0], q6[0][2], acc, sc[1]);
-  if constexpr (KS6 > 1) acc = mfma_f4f6<1>(ka[1], q6[1][2], acc, sc[1]);
+  acc = mfma_kq<FA, 0>(ka[0], q6[0][0], acc, sc[0]);
+  if constexpr (KS6 > 1) acc = mfma_kq<FA, 2>(ka[1], q6[1][0], acc, sc[0]);
+  acc = mfma_kq<FA, 1>(ka[0], q6[0][1], acc, sc[0]);
+  if constexpr (KS6 > 1) acc = mfma_kq<FA, 3>(ka[1], q6[1][1], acc, sc[0]);
+  acc = mfma_kq<FA, 0>(ka[0], q6[0][2], acc, sc[1]);
+  if constexpr (KS6 > 1) acc = mfma_kq<FA, 1>(ka[1], q6[1][2], acc, sc[1]);
   return acc;
+}
+
+// 32 INT4 codes (four packed words, channel k at bits 4k of word k / 8) as 32 fp6 e2m3
+// values c / 2, exact, in channel order: six words. The conversion is written out with
+// its result marked early-clobber: it writes part of its result before it has read all
+// of its sources, and these sources die at it.
+__device__ inline i32x6 fp6_key_slice(uint4 w) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  f32x16 s0, s1;  // element 2j: channel 2j, 2j + 1: channel 2j + 1
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const uint32_t lo = ws[m] & 0x0F0F0F0Fu, hi = (ws[m] >> 4) & 0x0F0F0F0Fu;  // channels 8m + 2b, + 1
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      s0[4 * m + b] = (float)((lo >> (8 * b)) & 0xFFu);
+      s1[4 * m + b] = (float)((hi >> (8 * b)) & 0xFFu);
+    }
+  }
+  i32x6 r;
+  asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(s0), "v"(s1), "v"(2.0f));
+  return r;
 }
 
 // fp4 key operand of 32 channels from two packed INT2 words (16 channels each, channel
@@ -369,12 +395,13 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   static_assert(TG == 0 || (!PERCH && TG % 32 == 0 && TG < D && NG <= kNS), "group-wise options");
   constexpr int HALF = D / 2;
   constexpr int KSTEPS = D / 32;  // int8 K-steps of 32 channels
-  // Per-token INT2 keys: QK^T on the scaled fp4 x fp6 MFMA (32x32x64, twice the K of the
-  // int8 MFMA per instruction at its rate): the codes as fp4 e2m1 (value code / 2, block
-  // scale 2), the rotated query as three fp6 e2m3 passes (a rounding, the rounding of its
-  // residual, the rounding of what is left), each with a power-of-two scale per lane and
-  // 32 channels, summed in one fp32 accumulator.
-  constexpr bool kF6 = BITS == 2 && !PERCH && TG == 0;
+  // Per-token keys: QK^T on the scaled MFMA (32x32x64, twice the K of the int8 MFMA per
+  // instruction at its rate): the codes as the values code / 2 (2-bit: fp4 e2m1, 4-bit:
+  // fp6 e2m3; key scale 2), the rotated query as three fp6 e2m3 passes (a rounding, the
+  // rounding of its residual, the rounding of what is left), each with a power-of-two
+  // scale per lane and 32 channels, summed in one fp32 accumulator.
+  constexpr bool kF6 = !PERCH && TG == 0;
+  constexpr int kFA = BITS == 2 ? 4 : 2;  // key operand format: fp4 e2m1, fp6 e2m3
   constexpr int KS6 = D / 64;  // fp6 K-steps of 64 channels (a lane holds 32 of each)
   constexpr int CBLK = D / 32;    // 32-channel output blocks
   constexpr int CPW = 32 / BITS;
@@ -390,6 +417,9 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   constexpr int VITEMS = (kBN / 2) * SEGS;  // current-value (token pair, segment) items per tile
   // items per thread (work counts below kThreads leave whole waves idle)
   constexpr int KUPT = (KUNITS + kThreads - 1) / kThreads;
+  // 4-bit keys on the fp6 path are staged 32 channels (two units) per thread by the first
+  // KPAIRS threads (the first wave of each SIMD finishes its block work first)
+  constexpr int KPAIRS = KUNITS / 2;
   // Cached values are staged by the first wave of each SIMD only (waves 0..3): the second
   // wave of a SIMD issues after the first and is the one that ends each step last.
   constexpr int kVST = kThreads / 2;
@@ -399,6 +429,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   static_assert(kStreams == 1, "one 32-query stream per wave");
   static_assert(KUNITS % 64 == 0 && VGROUPS % 64 == 0 && RITEMS % 64 == 0 && VITEMS % 64 == 0, "wave-uniform split");
   static_assert(KUPT <= RIPT && VGPT <= 2 * VRPT && RIPT <= 4 && VRPT <= 2, "staging registers");
+  static_assert(KPAIRS % 64 == 0 && KPAIRS <= kThreads / 2, "4-bit key pairs: whole waves");
   static_assert(kVST % 64 == 0 && kVST % 4 == 0, "value staging by whole waves, one token group per lane");
 
   const int tid = threadIdx.x;
@@ -564,7 +595,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     // query-side factors of the bias MFMA (key side in the tile parameters):
     //   (Delta_j z_j) * w + (Delta_j^2 / 64) * g - m - 65504 * mask_j
     if constexpr (kF6) {
-      const float lsum = encode_query_fp6<HALF>(qv, q6, q6sc);
+      const float lsum = encode_query_fp6<HALF, BITS>(qv, q6, q6sc);
       qs6 = lsum + xor32(lsum);
     }
     const float w = -A * (kF6 ? qs6 : (float)qs);
@@ -832,6 +863,13 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     if constexpr (decltype(k_c)::value == kCached) {
       // buffer loads: per-lane offsets are loop-invariant, the tile offset is uniform
       const uint32_t tok0 = (uint32_t)U * kBN;
+      if constexpr (kF6 && BITS == 4) {
+        const int kp = tid;  // unit pair: 32 channels of token kp / (D / 32)
+        if (kp < KPAIRS) {
+          const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs_kc, (uint32_t)kp * 16u, tok0 * KW * 4u, 0);
+          kpre[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      } else
 #pragma unroll
       for (int i = 0; i < KUPT; i++) {
         const uint32_t un = (uint32_t)min(tid + i * kThreads, KUNITS - 1);
@@ -890,6 +928,18 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     auto& ps = sm.prm[slot];
     const int nv = n_valid(U);
     if constexpr (decltype(k_c)::value == kCached) {
+      if constexpr (kF6 && BITS == 4) {
+        // fp6 rows: 32 channels (a unit pair) in 24 bytes
+        const int kp = tid;
+        if (kp < KPAIRS) {
+          const int tok = kp / (D / 32), pi = kp % (D / 32);
+          const i32x6 c = fp6_key_slice(kpre[0]);
+          uint2* dst = reinterpret_cast<uint2*>(&ks.c[tok][24 * pi]);
+          dst[0] = make_uint2((uint32_t)c[0], (uint32_t)c[1]);
+          dst[1] = make_uint2((uint32_t)c[2], (uint32_t)c[3]);
+          dst[2] = make_uint2((uint32_t)c[4], (uint32_t)c[5]);
+        }
+      } else
 #pragma unroll
       for (int i = 0; i < KUPT; i++) {
         const int un = tid + i * kThreads;
@@ -935,7 +985,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           dst[1] = make_uint4(res[4], res[5], res[6], res[7]);
         } else if constexpr (PERCH) {  // packed code slots
           *reinterpret_cast<uint4*>(&sm.kc(slot)[tok][16 * ui]) = lo;
-        } else if constexpr (kF6) {
+        } else if constexpr (kF6) {  // 2-bit keys (4-bit ones are staged above)
           // fp4 nibbles of channels 16 ui + 2 n (first word) and 16 ui + 2 n + 1 (second)
           const uint32_t w = kpre[i].x;
           *reinterpret_cast<uint2*>(&ks.c[tok][8 * ui]) = make_uint2(w & 0x33333333u, (w >> 2) & 0x33333333u);
@@ -1181,7 +1231,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // bf16 key rows (current), read from LDS ahead of their MFMAs.
   uint4 kbop;
   i32x4 kop[D / 16];
-  i32x8 kop6[kF6 ? KS6 : 1];  // fp4 key operands (4 of 8 words used)
+  i32x8 kop6[kF6 ? KS6 : 1];  // key operands (fp4: 4 of 8 words used, fp6: 6)
   int rk_slot = 0, rk_mb = 0;  // group-wise keys: the block whose key rows qk reads
   auto read_k = [&](int slot, int mb, auto k_c) KVQ_INLINE {
     const typename SM::KSlot& ks = sm.k[slot];
@@ -1200,12 +1250,20 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         else if constexpr (!kF6)
           kop[kk] = *reinterpret_cast<const i32x4*>(&ks.c[krow][HALF * h + 16 * kk]);
       }
-      if constexpr (kF6) {
+      if constexpr (kF6 && BITS == 2) {
         // fp4 rows: channel c at nibble c of the row (in kperm6 order per 32 channels)
 #pragma unroll
         for (int k6 = 0; k6 < KS6; k6++) {
           const uint4 w4 = *reinterpret_cast<const uint4*>(&ks.c[krow][(HALF * h + 32 * k6) / 2]);
           kop6[k6] = i32x8{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w, 0, 0, 0, 0};
+        }
+      } else if constexpr (kF6) {
+        // fp6 rows: 32 channels in 24 bytes, channel order
+#pragma unroll
+        for (int k6 = 0; k6 < KS6; k6++) {
+          const uint2* r = reinterpret_cast<const uint2*>(&ks.c[krow][3 * (HALF * h + 32 * k6) / 4]);
+          const uint2 a = r[0], b = r[1], c = r[2];
+          kop6[k6] = i32x8{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
         }
       }
     } else {  // fp16 rows: current-chunk keys (bf16)
@@ -1238,7 +1296,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     } else if constexpr (decltype(k_c)::value == kCached && kF6) {
       // S = sum_c q'_c code_c in fp32, pass by pass; the key scale 2^1 (E8M0 128) turns the
       // fp4 values code / 2 into the codes
-      sqh[SET] = __builtin_bit_cast(i32x16, qk_fp6(kop6, q6, q6sc));
+      sqh[SET] = __builtin_bit_cast(i32x16, qk_fp6<kFA>(kop6, q6, q6sc));
     } else if constexpr (decltype(k_c)::value == kCached) {
       // S = 256 S_hi + S_lo in one accumulator: the hi sums, a shift, then the lo sums
       i32x16 acc_s = {};
@@ -1493,12 +1551,16 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       if (!kLateV) read_v(slot0, 1);
       __builtin_amdgcn_sched_barrier(0);
       // the key staging (VALU and LDS writes) runs in the shadow of block 1's QK^T MFMAs
-      if (stage_k) store_k(U + 2, slot2, k_c);
+      // (4-bit keys on the fp6 path: at the end of the step, where their conversion's 32
+      // floats do not meet the live scores)
+      constexpr bool kLateK = kF6 && BITS == 4 && decltype(k_c)::value == kCached;
+      if (!kLateK && stage_k) store_k(U + 2, slot2, k_c);
       if (kEarlyK && T + 3 < n_t) load_k(U + 3, k_c);
       __builtin_amdgcn_sched_barrier(0);
       softmax(slot0, 1, set0, k_c, no);
       if (kLateV) read_v(slot0, 1);
       pv();
+      if (kLateK && stage_k) store_k(U + 2, slot2, k_c);
     } else {
       if (stage_k) store_k(U + 2, slot2, k_c);
       if (kEarlyK && T + 3 < n_t) load_k(U + 3, k_c);
@@ -1881,7 +1943,7 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
     float qsum;  // the sum of the query channels as the QK^T operands hold them
     if constexpr (kF6) {
       A = scale_l2;
-      const float lsum = encode_query_fp6<HALF>(qv, q6, q6sc);
+      const float lsum = encode_query_fp6<HALF, 2>(qv, q6, q6sc);
       qsum = lsum + xor32(lsum);
     } else {
       const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
@@ -2033,7 +2095,7 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
         i32x8 ka[KS6];
 #pragma unroll
         for (int k6 = 0; k6 < KS6; k6++) ka[k6] = fp4_key_operand(cur.k[mb][2 * k6], cur.k[mb][2 * k6 + 1]);
-        const f32x16 sf = qk_fp6(ka, q6, q6sc);
+        const f32x16 sf = qk_fp6<4>(ka, q6, q6sc);
 #pragma unroll
         for (int v = 0; v < 16; v++) sqf[v] = sf[v];
       } else {

@@ -874,3 +874,67 @@ def test_token_group_c40_sampled_rows():
     Or, PSr, PRr = run_oracle(x, w, rows=rows, heads=heads)
     assert_attention_close(_gather(O, heads, rows), Or, "c40_tgroup")
     assert_mass_close(_gather(PS, heads, rows), _gather(PR, heads, rows), PSr, PRr, "c40_tgroup")
+
+
+# Query magnitudes: the cached-key QK^T rounds the rotated query with power-of-two scales
+# taken from its own values (per query and 32 channels with 2-bit per-token keys, per
+# 32 queries with 4-bit keys), so scaled, tiny, zero and one-channel-dominated queries
+# must all stay within the tolerance of the oracle.
+def _scale_rows(x, f):
+    q = synth.bf16_bits_to_f32(x["q"]).astype(np.float32)
+    return dict(x, q=synth.f32_to_bf16_bits(f(q)))
+
+
+def _hot_channel(q):
+    q = q.copy()
+    q[..., 3] *= 50.0
+    return q
+
+
+def _zero_rows(q):
+    q = q.copy()
+    q[:, :, : min(40, q.shape[2] // 2)] = 0.0
+    q[:, :, -1] = 0.0
+    return q
+
+
+@pytest.mark.parametrize("n_q", [300, 16])  # main kernel; few-query path
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("case,k_had", [("x8", True), ("x2^-20", True), ("zero rows", True),
+                                        ("hot channel", True), ("hot channel", False)])
+def test_query_magnitudes(case, k_had, bits, n_q):
+    w = synth.Workload("qmag", B=1, H=2, d=128, n_q=n_q, chunk_len=200, n_chunks=3, bits=bits, seed=21)
+    print(f"attn query magnitudes: {case}, hadamard={k_had}, bits={bits}, n_q={n_q}", flush=True)
+    f = {"x8": lambda q: q * 8.0, "x2^-20": lambda q: q * 2.0 ** -20, "zero rows": _zero_rows,
+         "hot channel": _hot_channel}[case]
+    x = _scale_rows(synth.draw_all(w), f)
+    O, PS, PR = run_gpu(x, w, k_had=k_had)
+    Or, PSr, PRr = run_oracle(x, w, k_had=k_had)
+    assert_attention_close(O, Or, f"query {case} had={k_had} b{bits}")
+    assert_mass_close(PS, PR, PSr, PRr, f"query {case} had={k_had} b{bits}")
+
+
+def test_inline_tensors_and_dirty_workspace():
+    # inputs made inline in make_args, a workspace full of NaN: the call must read its own
+    # inputs (which args keeps alive) and write every partial record it combines
+    w = synth.WORKLOADS["tiny"]
+    print("attn tiny: inline input tensors, NaN-filled workspace", flush=True)
+    x = synth.draw_all(w)
+    kvq = _kvq()
+    kf, vf = lib_formats(w)
+    kwin = kvq.pack_window(dev(x["k_cache"]), w.chunk_len, kf)
+    vwin = kvq.pack_window(dev(x["v_cache"]), w.chunk_len, vf)
+    o = torch.empty((w.B, w.H, w.n_q, w.d), dtype=torch.float32, device="cuda")
+    ms = torch.empty((w.B, w.H, w.n_q), dtype=torch.float32, device="cuda")
+    mr = torch.empty_like(ms)
+    args = kvq.make_args(dev(x["q"]), dev(x["k_cur"]), dev(x["v_cur"]), kwin, vwin, w.chunk_len, w.n_chunks, kf, vf,
+                         o=o, mass_s=ms, mass_r=mr)
+    ws = kvq.attach_workspace(args)
+    assert ws is not None, "the tiny shape runs split"
+    for _ in range(2):
+        ws.view(torch.float32).fill_(float("nan"))
+        kvq.jb_attn_fwd(args)
+        torch.cuda.synchronize()
+        Or, PSr, PRr = run_oracle(x, w)
+        assert_attention_close(o.cpu().numpy(), Or, "tiny inline, dirty workspace")
+        assert_mass_close(ms.cpu().numpy(), mr.cpu().numpy(), PSr, PRr, "tiny inline, dirty workspace")

@@ -32,9 +32,18 @@ FP6_PASSES = 3                   # query passes of the fp4 x fp6 QK^T
 
 
 def fp6_qk(w, decode):
-    """Whether the attention kernel runs QK^T on the scaled fp4 x fp6 MFMA: 2-bit
-    per-token keys in the main kernel (not the few-query path, not group-wise keys)."""
-    return w.bits == 2 and w.k_granularity == "token" and not decode
+    """Whether the attention kernel runs QK^T on the scaled fp4/fp6 x fp6 MFMA: per-token
+    keys, 2-bit in both kernels, 4-bit in the main kernel (the few-query path keeps int8)."""
+    return w.k_granularity == "token" and (w.bits == 2 or not decode)
+
+
+def path_dtype(w, decode):
+    """The arithmetic of the path: QK^T operands, then the bias / PV MFMAs' fp16."""
+    if w.k_granularity == "token_group":
+        return "fp16"
+    if fp6_qk(w, decode):
+        return "fp4xfp6+fp16" if w.bits == 2 else "fp6xfp6+fp16"
+    return "int8+fp16"
 
 
 def mixed_peak():
@@ -360,8 +369,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp4xfp6+fp16" if fp6_qk(w, decode) else
-                  "fp16" if w.k_granularity == "token_group" else "int8+fp16"),
+        "dtype": path_dtype(w, decode),
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} d={w.d}, current chunk {w.n_q} tokens, window "
                                f"{w.n_chunks}x{w.chunk_len} cached tokens, INT{w.bits} {gran_text(w, w.k_granularity)} K, "
@@ -383,7 +391,7 @@ def main():
                      {"bound": "hbm", "achieved": round(algo_bytes / (attn_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(algo_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
         | ({"peak_mixed": round(mixed_peak(), 1), "frac_mixed": round(achieved / mixed_peak(), 4)}
-           if fp6_qk(w, decode) else {})
+           if fp6_qk(w, decode) and not decode else {})
         | {"traffic": (round(traffic) if traffic is not None else None),
            "algorithmic_bytes": algo_bytes, "kernel_source_sha256_16": kernel_source_hash(),
            "mfma_busy": ctr.get("mfma_busy"), "valu_busy": ctr.get("valu_busy")},

@@ -31,18 +31,21 @@ PEAK_FP6_TFLOPS = 10100.0        # MI355X dense fp6/fp4 MFMA
 FP6_PASSES = 3                   # query passes of the fp4 x fp6 QK^T
 
 
-def fp6_qk(w, decode):
+def fp6_qk(w, decode, correction=1):
     """Whether the attention kernel runs QK^T on the scaled fp4/fp6 x fp6 MFMA: per-token
-    keys, 2-bit in both kernels, 4-bit in the main kernel (the few-query path keeps int8)."""
+    keys, 2-bit in both kernels, 4-bit in the main kernel (the few-query path keeps int8);
+    group-wise keys in two 64-channel groups without the exact correction."""
+    if w.k_granularity == "token_group":
+        return w.group == 64 and w.d == 128 and correction != 2 and not decode
     return w.k_granularity == "token" and (w.bits == 2 or not decode)
 
 
-def path_dtype(w, decode):
+def path_dtype(w, decode, correction=1):
     """The arithmetic of the path: QK^T operands, then the bias / PV MFMAs' fp16."""
+    if fp6_qk(w, decode, correction):
+        return "fp4xfp6+fp16" if w.bits == 2 else "fp6xfp6+fp16"
     if w.k_granularity == "token_group":
         return "fp16"
-    if fp6_qk(w, decode):
-        return "fp4xfp6+fp16" if w.bits == 2 else "fp6xfp6+fp16"
     return "int8+fp16"
 
 
@@ -213,7 +216,7 @@ def measure_other(key, launches=OTHER_LAUNCHES, warmup=3):
         rec.update({"bound": "hbm", "GBps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)})
     else:
         rec.update({"bound": "mfma", "frac": round(w.flops() / (med * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 4)})
-        if fp6_qk(w, decode):
+        if fp6_qk(w, decode, correction):
             rec["frac_mixed"] = round(w.flops() / (med * 1e-3) / 1e12 / mixed_peak(), 4)
     del ws, q, kr, vr, kwin, vwin, o, ms, mr
     torch.cuda.empty_cache()
@@ -369,7 +372,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": path_dtype(w, decode),
+        "dtype": path_dtype(w, decode, args.correction),
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} d={w.d}, current chunk {w.n_q} tokens, window "
                                f"{w.n_chunks}x{w.chunk_len} cached tokens, INT{w.bits} {gran_text(w, w.k_granularity)} K, "
@@ -391,7 +394,7 @@ def main():
                      {"bound": "hbm", "achieved": round(algo_bytes / (attn_ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(algo_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
         | ({"peak_mixed": round(mixed_peak(), 1), "frac_mixed": round(achieved / mixed_peak(), 4)}
-           if fp6_qk(w, decode) and not decode else {})
+           if fp6_qk(w, decode, args.correction) and not decode else {})
         | {"traffic": (round(traffic) if traffic is not None else None),
            "algorithmic_bytes": algo_bytes, "kernel_source_sha256_16": kernel_source_hash(),
            "mfma_busy": ctr.get("mfma_busy"), "valu_busy": ctr.get("valu_busy")},

@@ -280,7 +280,7 @@ struct Smem<D, true, 0> : SmemSlots<D> {
 // 2^ex > max|.| / 7.5, passes 1 and 2 round what is left the same way. Writes the
 // operands q6[k6][pass] and their E8M0 scale bytes (passes 0 and 1 of K-step k6 in bytes
 // 2 k6 and 2 k6 + 1 of sc[0], pass 2 in byte k6 of sc[1]); returns the lane's sum of the
-// rounded channels.
+// rounded channels per K-step (the _slices form) or in all (encode_query_fp6).
 // The rounding is the hardware conversion (32 floats / scale to packed e2m3, to nearest
 // even, saturating at 7.5; packed element 2j from the first operand's j-th value, 2j + 1
 // from the second's) and its inverse gives the rounded values. Every pass reads its
@@ -288,14 +288,15 @@ struct Smem<D, true, 0> : SmemSlots<D> {
 // conversion's result registers: it writes part of its result before it has read all
 // of its sources.
 template <int HALF, int BITS>
-__device__ KVQ_INLINE float encode_query_fp6(const float (&qv)[HALF], i32x8 (&q6)[HALF / 32][3], uint32_t (&sc)[2]) {
-  float qsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < HALF; i++) qsum += qv[i];
+__device__ KVQ_INLINE void encode_query_fp6_slices(const float (&qv)[HALF], i32x8 (&q6)[HALF / 32][3], uint32_t (&sc)[2],
+                                                   float (&ksum)[HALF / 32]) {
   sc[0] = 0u;
   sc[1] = 0u;
 #pragma unroll
   for (int k6 = 0; k6 < HALF / 32; k6++) {
+    float qsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) qsum += qv[32 * k6 + i];
     f32x16 s0, s1;  // element 2j: channel 32 k6 + kslot(2j); 2j + 1: kslot(2j + 1)
 #pragma unroll
     for (int j = 0; j < 16; j++) {
@@ -326,8 +327,19 @@ __device__ KVQ_INLINE float encode_query_fp6(const float (&qv)[HALF], i32x8 (&q6
     // the sum of the rounded channels: the sum of q' minus what the passes left
 #pragma unroll
     for (int j = 0; j < 16; j++) qsum -= s0[j] + s1[j];
+    ksum[k6] = qsum;
   }
-  return qsum;
+}
+
+// encode_query_fp6_slices, returning the lane's sum of the rounded channels.
+template <int HALF, int BITS>
+__device__ KVQ_INLINE float encode_query_fp6(const float (&qv)[HALF], i32x8 (&q6)[HALF / 32][3], uint32_t (&sc)[2]) {
+  float ks[HALF / 32];
+  encode_query_fp6_slices<HALF, BITS>(qv, q6, sc, ks);
+  float t = 0.f;
+#pragma unroll
+  for (int k6 = 0; k6 < HALF / 32; k6++) t += ks[k6];
+  return t;
 }
 
 // S = sum_c q~_c code_c of one 32x32 block in fp32: six scaled MFMAs (three query passes
@@ -402,6 +414,11 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // scale per lane and 32 channels, summed in one fp32 accumulator.
   constexpr bool kF6 = !PERCH && TG == 0;
   constexpr int kFA = BITS == 2 ? 4 : 2;  // key operand format: fp4 e2m1, fp6 e2m3
+  // Group-wise keys in two 64-channel groups (Taylor or no correction): the same QK^T
+  // with one accumulator per group, a 64-channel K-step being one group (the lane halves
+  // swap query channels so that K-step g holds group g), the codes as fp4 / fp6 rows, and
+  // the logit sum_g (Delta_jg A) S_g + c with the groups' zero points in the bias.
+  constexpr bool kF6G = TG == 64 && NG == 2 && !EXACT && !PERCH;
   constexpr int KS6 = D / 64;  // fp6 K-steps of 64 channels (a lane holds 32 of each)
   constexpr int CBLK = D / 32;    // 32-channel output blocks
   constexpr int CPW = 32 / BITS;
@@ -448,9 +465,9 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // ---------------- query operands ----------------
   i32x4 qhi[KSTEPS], qlo[KSTEPS];  // int8 hi/lo of q_f (cached keys), or the bf16 query
   // group-wise keys: the rotated query as fp16 hi + lo, in the staged key rows' channel order
-  f16x8 q16h[TG > 0 ? D / 16 : 1], q16l[TG > 0 ? D / 16 : 1];
+  f16x8 q16h[TG > 0 && !kF6G ? D / 16 : 1], q16l[TG > 0 && !kF6G ? D / 16 : 1];
   f16x8 qbias;                     // query operand of the bias MFMA
-  i32x8 q6[kF6 ? KS6 : 1][3];      // fp6 query operands: K-step, pass
+  i32x8 q6[kF6 || kF6G ? KS6 : 1][3];  // fp6 query operands: K-step, pass
   uint32_t q6sc[2] = {0u, 0u};     // their E8M0 scale bytes
   float m_run = -INFINITY;         // reference max (log2 units); -inf until the first block
   float a_st = 0.f;                // A of this wave's stream
@@ -507,7 +524,22 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   auto build_query = [&]() KVQ_INLINE {
     float qv[HALF];
     rotated_query(qv);
-    if constexpr (TG > 0) {
+    float qgrp[2] = {0.f, 0.f};  // kF6G: the rounded query's sum over each group
+    if constexpr (kF6G) {
+      // K-step g holds group g: lane half h takes channels 64 g + 32 h + e, swapping half
+      // of its channels with the partner lane
+      float qx[HALF];
+#pragma unroll
+      for (int i = 0; i < 32; i++) {
+        const float r = xor32(h ? qv[i] : qv[32 + i]);
+        qx[i] = h ? r : qv[i];
+        qx[32 + i] = h ? qv[32 + i] : r;
+      }
+      float ks[2];
+      encode_query_fp6_slices<HALF, BITS>(qx, q6, q6sc, ks);
+      qgrp[0] = ks[0] + xor32(ks[0]);
+      qgrp[1] = ks[1] + xor32(ks[1]);
+    } else if constexpr (TG > 0) {
       // position 16u + 2k + b of a staged key row holds channel 16u + k + 8b (the pair
       // order of the code unpack); lane half h, K-step t reads positions HALF h + 8t ..
 #pragma unroll
@@ -531,7 +563,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) mxa = fmaxf(mxa, __shfl_xor(mxa, sh));  // stream-wide max
     const float inv = mxa > 0.f ? kQFix / mxa : 0.f;
-    const float A = kF6 ? scale_l2 : mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
+    const float A = kF6 || kF6G ? scale_l2 : mxa > 0.f ? scale_l2 * (mxa / kQFix) : 0.f;
     int qs = 0;
     float qs6 = 0.f;  // fp6 path: the sum of the rounded query's channels
     if constexpr (!kF6) {
@@ -638,6 +670,19 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         qsl[k0 + (k0 >= 8 ? 3 : 0)] = yh;
         qsl[k0 + 1 + (k0 + 1 >= 8 ? 3 : 0)] = yl;
         qsl[k0 + 2 + (k0 + 2 >= 8 ? 3 : 0)] = yh;
+      }
+      if constexpr (kF6G) {
+        // the zero points of groups 0 and 1, -A Q_g against Delta_jg z_jg: slots 6, 7, 11
+        // and 12, 13, 14 as (hi, lo, hi)
+        _Float16 zh, zl;
+        split16(-A * qgrp[0], zh, zl);
+        qsl[6] = zh;
+        qsl[7] = zl;
+        qsl[11] = zh;
+        split16(-A * qgrp[1], zh, zl);
+        qsl[12] = zh;
+        qsl[13] = zl;
+        qsl[14] = zh;
       }
 #pragma unroll
       for (int e = 0; e < 8; e++) qbias[e] = h ? qsl[8 + e] : qsl[e];
@@ -845,6 +890,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // group-wise: the NG fp16 steps of key tid & 63 (groups 0, 1 in .x, groups 2, 3 in .y),
   // and the step and zero point of this thread's 16-channel key unit
   uint2 gk_d = make_uint2(0, 0);
+  uint2 gk_z = make_uint2(0, 0);  // kF6G: the NG zero points of key tid & 63
   uint32_t uk_d = 0, uk_z = 0;
   uint2 gv_z0 = make_uint2(0, 0), gv_z1 = make_uint2(0, 0), gv_d0 = make_uint2(0, 0), gv_d1 = make_uint2(0, 0);
   auto load_pairs = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t tok, uint32_t tok0) KVQ_INLINE -> uint2 {
@@ -863,7 +909,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     if constexpr (decltype(k_c)::value == kCached) {
       // buffer loads: per-lane offsets are loop-invariant, the tile offset is uniform
       const uint32_t tok0 = (uint32_t)U * kBN;
-      if constexpr (kF6 && BITS == 4) {
+      if constexpr ((kF6 || kF6G) && BITS == 4) {
         const int kp = tid;  // unit pair: 32 channels of token kp / (D / 32)
         if (kp < KPAIRS) {
           const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs_kc, (uint32_t)kp * 16u, tok0 * KW * 4u, 0);
@@ -881,7 +927,11 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           kpre[i].x = __builtin_amdgcn_raw_buffer_load_b32(rs_kc, un * 4u, tok0 * KW * 4u, 0);
         }
       }
-      if constexpr (TG > 0) {
+      if constexpr (kF6G) {
+        const uint32_t j = (uint32_t)(tid & (kBN - 1));
+        gk_d = load_pairs(rs_ks, j, tok0);
+        gk_z = load_pairs(rs_kz, j, tok0);
+      } else if constexpr (TG > 0) {
         const uint32_t j = (uint32_t)(tid & (kBN - 1));
         gk_d = load_pairs(rs_ks, j, tok0);
         const uint32_t un = (uint32_t)min(tid, KUNITS - 1);
@@ -928,7 +978,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     auto& ps = sm.prm[slot];
     const int nv = n_valid(U);
     if constexpr (decltype(k_c)::value == kCached) {
-      if constexpr (kF6 && BITS == 4) {
+      if constexpr ((kF6 || kF6G) && BITS == 4) {
         // fp6 rows: 32 channels (a unit pair) in 24 bytes
         const int kp = tid;
         if (kp < KPAIRS) {
@@ -953,7 +1003,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           const uint32_t w0 = kpre[i].x, w1 = kpre[i].y;
           lo = make_uint4(w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu);
         }
-        if constexpr (TG > 0) {
+        if constexpr (TG > 0 && !kF6G) {
           // fp16 Delta (code - z) of channels 16 ui + k (low half) and 16 ui + k + 8 (high)
           // at positions 16 ui + 2k, + 1: (1024 + code) - (1024 + z) is exact in fp16
           uint32_t a[8];
@@ -985,7 +1035,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           dst[1] = make_uint4(res[4], res[5], res[6], res[7]);
         } else if constexpr (PERCH) {  // packed code slots
           *reinterpret_cast<uint4*>(&sm.kc(slot)[tok][16 * ui]) = lo;
-        } else if constexpr (kF6) {  // 2-bit keys (4-bit ones are staged above)
+        } else if constexpr (kF6 || kF6G) {  // 2-bit keys (4-bit ones are staged above)
           // fp4 nibbles of channels 16 ui + 2 n (first word) and 16 ui + 2 n + 1 (second)
           const uint32_t w = kpre[i].x;
           *reinterpret_cast<uint2*>(&ks.c[tok][8 * ui]) = make_uint2(w & 0x33333333u, (w >> 2) & 0x33333333u);
@@ -997,7 +1047,13 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       if constexpr (PERCH) {
         if (tid < D / 4) reinterpret_cast<uint4*>(&ps.dka[0][0])[tid] = gpre;
       }
-      if constexpr (TG > 0) {
+      if constexpr (kF6G) {
+        // Delta_jg A of each group (0 for padding keys), one row per group, M-row order
+        if (wave < NG) {
+          const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
+          ps.dka[wave][r] = lane < nv ? half_bits_to_f32(pair_bits(gk_d, wave)) * scale_l2 : 0.f;
+        }
+      } else if constexpr (TG > 0) {
         // per-group steps Delta_jg as fp16 bits (0 for padding keys), one row per group,
         // M-row order, in the per-key table's storage
         if (wave < NG) {
@@ -1037,6 +1093,17 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
               for (int e = 0; e < 3; e++) {
                 const int k = 3 * t + e, sl = k + (k >= 8 ? 3 : 0);
                 ksl[sl >> 1] |= v3[e] << (16 * (sl & 1));
+              }
+              if constexpr (kF6G) {
+                // the zero point Delta_jg z_jg of group t as (hi, hi, lo) at slots 6, 7, 11
+                // (t = 0) or 12, 13, 14 (t = 1)
+                _Float16 zh, zl;
+                split16(dk * half_bits_to_f32(pair_bits(gk_z, t)), zh, zl);
+                const uint32_t zhb = __builtin_bit_cast(uint16_t, zh), zlb = __builtin_bit_cast(uint16_t, zl);
+                const int sz[3] = {t == 0 ? 6 : 12, t == 0 ? 7 : 13, t == 0 ? 11 : 14};
+                const uint32_t z3[3] = {zhb, zhb, zlb};
+#pragma unroll
+                for (int e = 0; e < 3; e++) ksl[sz[e] >> 1] |= z3[e] << (16 * (sz[e] & 1));
               }
             }
           } else {
@@ -1222,6 +1289,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
 
   f32x16 acc[CBLK];
   i32x16 sqh[1];
+  i32x16 sqg1[1];  // kF6G: group 1's sums (group 0's in sqh)
   f32x16 cb[1];
   uint32_t pb[2][4];
 #pragma unroll
@@ -1231,13 +1299,27 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // bf16 key rows (current), read from LDS ahead of their MFMAs.
   uint4 kbop;
   i32x4 kop[D / 16];
-  i32x8 kop6[kF6 ? KS6 : 1];  // key operands (fp4: 4 of 8 words used, fp6: 6)
+  i32x8 kop6[kF6 || kF6G ? KS6 : 1];  // key operands (fp4: 4 of 8 words used, fp6: 6)
   int rk_slot = 0, rk_mb = 0;  // group-wise keys: the block whose key rows qk reads
   auto read_k = [&](int slot, int mb, auto k_c) KVQ_INLINE {
     const typename SM::KSlot& ks = sm.k[slot];
     const int krow = 32 * mb + mrow_key(col);
     kbop = sm.prm[slot].kb[32 * mb + col][h];
-    if constexpr (decltype(k_c)::value == kCached && TG > 0) {
+    if constexpr (decltype(k_c)::value == kCached && kF6G) {
+      // K-step g is group g: this lane half's 32 channels 64 g + 32 h .. (fp4 rows: 16
+      // bytes; fp6 rows: 24)
+#pragma unroll
+      for (int g = 0; g < 2; g++) {
+        if constexpr (BITS == 2) {
+          const uint4 w4 = *reinterpret_cast<const uint4*>(&ks.c[krow][32 * g + 16 * h]);
+          kop6[g] = i32x8{(int)w4.x, (int)w4.y, (int)w4.z, (int)w4.w, 0, 0, 0, 0};
+        } else {
+          const uint2* r = reinterpret_cast<const uint2*>(&ks.c[krow][48 * g + 24 * h]);
+          const uint2 a = r[0], b = r[1], c = r[2];
+          kop6[g] = i32x8{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
+        }
+      }
+    } else if constexpr (decltype(k_c)::value == kCached && TG > 0) {
       // group-wise keys: qk reads the fp16 key rows one K-step ahead of their MFMAs
       rk_slot = slot;
       rk_mb = mb;
@@ -1278,7 +1360,18 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       const f32x16 zf = {};
       cb[SET] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kbop), qbias, zf, 0, 0, 0);
     }
-    if constexpr (decltype(k_c)::value == kCached && TG > 0) {
+    if constexpr (decltype(k_c)::value == kCached && kF6G) {
+      // S_g = sum over group g of q~_c code_c: one three-pass chain per group
+      f32x16 s0 = {}, s1 = {};
+      s0 = mfma_kq<kFA, 0>(kop6[0], q6[0][0], s0, q6sc[0]);
+      s1 = mfma_kq<kFA, 2>(kop6[1], q6[1][0], s1, q6sc[0]);
+      s0 = mfma_kq<kFA, 1>(kop6[0], q6[0][1], s0, q6sc[0]);
+      s1 = mfma_kq<kFA, 3>(kop6[1], q6[1][1], s1, q6sc[0]);
+      s0 = mfma_kq<kFA, 0>(kop6[0], q6[0][2], s0, q6sc[1]);
+      s1 = mfma_kq<kFA, 1>(kop6[1], q6[1][2], s1, q6sc[1]);
+      sqh[SET] = __builtin_bit_cast(i32x16, s0);
+      sqg1[SET] = __builtin_bit_cast(i32x16, s1);
+    } else if constexpr (decltype(k_c)::value == kCached && TG > 0) {
       // S = k_hat' . (q'_hi + q'_lo) on fp16 MFMA, fp32 accumulation, K-step by K-step
       // (each key operand is read one K-step ahead and used by the hi and the lo MFMA)
       const uint16_t* krow = &sm.k[rk_slot].kr[32 * rk_mb + mrow_key(col)][HALF * h];
@@ -1348,7 +1441,21 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // Logits (log2 units; they carry -m through the bias) of block mb of tile U from SET.
   auto logits = [&](int slot, int mb, auto set_c, auto k_c, float* x) KVQ_INLINE {
     constexpr int SET = decltype(set_c)::value;
-    if constexpr (decltype(k_c)::value == kCached && TG > 0) {
+    if constexpr (decltype(k_c)::value == kCached && kF6G) {
+      const float* d0 = sm.prm[slot].dka[0];
+      const float* d1 = sm.prm[slot].dka[1];
+#pragma unroll
+      for (int v4 = 0; v4 < 4; v4++) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&d0[32 * mb + 8 * v4 + 4 * h]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&d1[32 * mb + 8 * v4 + 4 * h]);
+        const float da[4] = {a4.x, a4.y, a4.z, a4.w}, db[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+          const int v = 4 * v4 + b;
+          x[v] = fmaf(da[b], __int_as_float(sqh[SET][v]), fmaf(db[b], __int_as_float(sqg1[SET][v]), cb[SET][v]));
+        }
+      }
+    } else if constexpr (decltype(k_c)::value == kCached && TG > 0) {
 #pragma unroll
       for (int v = 0; v < 16; v++) x[v] = fmaf(scale_l2, __int_as_float(sqh[SET][v]), cb[SET][v]);
       if constexpr (EXACT) {
@@ -1537,7 +1644,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       // the compiler from sinking them): values under the softmax, keys under the PV
       // (group-wise keys read a block's values after its softmax: their fp16 query halves
       // take the registers)
-      constexpr bool kLateV = TG > 0 && decltype(k_c)::value == kCached;
+      constexpr bool kLateV = TG > 0 && !kF6G && decltype(k_c)::value == kCached;
       read_k(slot0, 0, k_c);
       qk(set0, k_c);
       if (!kLateV) read_v(slot0, 0);
@@ -1553,7 +1660,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
       // the key staging (VALU and LDS writes) runs in the shadow of block 1's QK^T MFMAs
       // (4-bit keys on the fp6 path: at the end of the step, where their conversion's 32
       // floats do not meet the live scores)
-      constexpr bool kLateK = kF6 && BITS == 4 && decltype(k_c)::value == kCached;
+      constexpr bool kLateK = (kF6 || kF6G) && BITS == 4 && decltype(k_c)::value == kCached;
       if (!kLateK && stage_k) store_k(U + 2, slot2, k_c);
       if (kEarlyK && T + 3 < n_t) load_k(U + 3, k_c);
       __builtin_amdgcn_sched_barrier(0);

@@ -2156,6 +2156,14 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
 #pragma unroll
   for (int c = 0; c < CBLK; c++) acc[c] = f32x16{};
   uint32_t pb[2][4];
+  // the value code field mask in a vector register, so that the unpack takes one and-or
+  // per pair (with two literals it would take an and and an or); 2-bit pair i of a value
+  // word sits at bit 8 h + 2 i for this lane half
+  uint32_t vmask = BITS == 2 ? 0x00030003u : 0x000F000Fu;
+  asm volatile("" : "+v"(vmask));
+  uint32_t vsh[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) vsh[i] = (uint32_t)(8 * h + 2 * i);
 
   // two waves per SIMD (at most 256 registers) hide each other's load latency; holding a
   // second tile's operands in registers would cost that occupancy
@@ -2289,7 +2297,7 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
           for (int c = 0; c < CBLK; c++) {
             uint32_t t;
             if constexpr (BITS == 2) {
-              t = (cur.v[c][g] >> (8 * h)) & 0x00FF00FFu;
+              t = cur.v[c][g];  // pair i: bits 8 h + 2 i (one shift, one and-or per pair)
             } else {
               const uint32_t w0 = cur.v[c][2 * g], w1 = cur.v[c][2 * g + 1];
               t = h ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
@@ -2297,8 +2305,8 @@ __global__ __launch_bounds__(64, 2) void jb_decode_kernel(const Params p, const 
             uint32_t res[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-              const uint32_t a = BITS == 2 ? (((t >> (2 * i)) & 0x00030003u) | 0x64006400u)
-                                           : (((t >> (4 * i)) & 0x000F000Fu) | 0x64006400u);
+              const uint32_t a = BITS == 2 ? (((t >> vsh[i]) & vmask) | 0x64006400u)
+                                           : (((t >> (4 * i)) & vmask) | 0x64006400u);
               const f16x2 cz = __builtin_bit_cast(f16x2, a) + __builtin_bit_cast(f16x2, zz[i]);
               res[i] = __builtin_bit_cast(uint32_t, cz * __builtin_bit_cast(f16x2, dd[i]));
             }

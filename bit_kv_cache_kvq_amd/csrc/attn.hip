@@ -1704,9 +1704,15 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   };
 
   // ---------------- this workgroup's tiles: cached ones, then current ones ----------------
-  // Share sp of the tile sequence (cached tiles 0..n_ct-1, then the current chunk's).
-  const int n_tt = n_ct + n_rt;
-  const int t_beg = (int)((long long)sp * n_tt / p.n_split), t_end = (int)((long long)(sp + 1) * n_tt / p.n_split);
+  // Share sp of the tile sequence (cached tiles 0..n_ct-1, then the current chunk's), the
+  // shares cut at equal cost: a current tile (bf16 keys and values read from memory, bf16
+  // QK^T on eight MFMAs per block) takes about 4/3 of a cached tile's time.
+  const long long cost_all = 3LL * n_ct + 4LL * n_rt;
+  auto cut = [&](int s) KVQ_INLINE -> int {
+    const long long x = (long long)s * cost_all / p.n_split;
+    return x <= 3LL * n_ct ? (int)(x / 3) : n_ct + (int)((x - 3LL * n_ct) / 4);
+  };
+  const int t_beg = cut(sp), t_end = cut(sp + 1);
   const int c_beg = min(t_beg, n_ct), c_end = min(t_end, n_ct);
   const int r_beg = max(t_beg, n_ct) - n_ct, r_end = max(t_end, n_ct) - n_ct;
   if (c_end > c_beg) {

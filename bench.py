@@ -75,6 +75,7 @@ OTHERS = {
     "c40_tgroup32": ("c40_tgroup", {"group": 32}, 1),
     "c40_tgroup64": ("c40_tgroup", {"group": 64}, 1),
     "c40_exact": ("c40", {}, 2),
+    "c40_perch_exact": ("c40_perch", {}, 2),
 }
 OTHER_LAUNCHES = 10
 

@@ -15,22 +15,30 @@
 //  * Scores are computed transposed, S^T = K Q^T: keys are the MFMA M dimension and
 //    each lane owns one query (lane l^32 holds the other half of every 32-key block),
 //    so the softmax state of a query lives in one lane pair.
-//  * Cached QK^T runs on int8 MFMA (v_mfma_i32_32x32x32_i8). The rotated query
-//    q' = H q is a 16-bit fixed-point integer q_f (one scale sigma per wave) split into
-//    signed bytes q_f = 256 hi + lo; the key operand is the raw code, unpacked once per
-//    workgroup into LDS; S = 256 S_hi + S_lo is exact in int32.
+//  * Cached QK^T with per-token keys runs on the scaled MFMA
+//    (v_mfma_scale_f32_32x32x64_f8f6f4): the key operand is the raw code, as fp4 e2m1
+//    (2-bit codes, value code / 2 with a key scale of 2) or fp6 e2m3 (4-bit codes),
+//    unpacked once per workgroup into LDS; the rotated query q' = H q enters as three
+//    fp6 e2m3 passes (a rounding, then roundings of what is left), each with a
+//    power-of-two scale per lane and 32 channels, summed in one fp32 accumulator.
+//    Group-wise keys of 64 channels run the same contraction with one accumulator per
+//    group; group-wise keys of 32 channels (and group-wise keys with the exact
+//    correction) are dequantized to fp16 in the staging and meet the query as fp16
+//    hi + lo parts on fp16 MFMA.
 //  * The zero point, the correction, the reference max and the padding mask enter
 //    through one fp16 MFMA per block whose key operand holds Delta_j z_j, Delta_j^2
-//    (hi/lo fp16 pairs), 1 and the mask, and whose query operand holds -A sum(q_f),
-//    -G, -m and a large negative constant. In log2 units the logit is
-//    x = (Delta_j A) S + c with A = s sigma log2 e and G = s^2 |q'|^2 / 24 log2 e, so a
-//    score costs a convert, one fma and one exp2 (the int8 MFMAs accumulate the hi sums,
-//    shift them by 8 and add the lo sums in the same int32 accumulator).
-//  * Keys quantized per channel over token groups (Delta_gc, z_gc): at each group's
-//    first tile the wave rescales its rotated query by the group's steps, re-quantizes
-//    it (scale a_ch) and folds the group's zero-point and correction terms into a
-//    per-query constant carried by the bias MFMA; the logit is x = a_ch S + c. The
-//    rotated queries stay in LDS (16-bit fixed point) for the whole cached window.
+//    (hi/lo fp16 pairs), 1 and the mask, and whose query operand holds -A times the
+//    query's channel sum (as the QK^T operands hold it), -G, -m and a large negative
+//    constant. In log2 units the logit is x = (Delta_j A) S + c with A = s log2 e and
+//    G = s^2 |q'|^2 / 24 log2 e, so a score costs one fma and one exp2.
+//  * Keys quantized per channel over token groups (Delta_gc, z_gc) run QK^T on int8
+//    MFMA (v_mfma_i32_32x32x32_i8): at each group's first tile the wave rescales its
+//    rotated query by the group's steps, q~ = q' Delta_g, quantizes it to 16-bit
+//    fixed point (one scale a_ch per wave) split into signed bytes hi, lo (the int32
+//    sum 256 S_hi + S_lo is exact), and folds the group's zero-point and correction
+//    terms into a per-query constant carried by the bias MFMA; the logit is
+//    x = a_ch S + c. The rotated queries stay in LDS (16-bit fixed point) for the
+//    whole cached window.
 //  * The reference max m starts at the first block's maximum plus a headroom of 2^2 (a
 //    larger headroom pushes keys a few binades below the max into fp16 subnormals) and
 //    stays fixed while every p = exp2(x) fits fp16 (checked by the fp16 row sum of each
@@ -463,7 +471,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   const float scale_l2 = p.s * kLog2e;  // softmax scale in log2 units
 
   // ---------------- query operands ----------------
-  i32x4 qhi[KSTEPS], qlo[KSTEPS];  // int8 hi/lo of q_f (cached keys), or the bf16 query
+  i32x4 qhi[KSTEPS], qlo[KSTEPS];  // int8 hi/lo of q_f (per-channel keys), or the bf16 query
   // group-wise keys: the rotated query as fp16 hi + lo, in the staged key rows' channel order
   f16x8 q16h[TG > 0 && !kF6G ? D / 16 : 1], q16l[TG > 0 && !kF6G ? D / 16 : 1];
   f16x8 qbias;                     // query operand of the bias MFMA
@@ -693,7 +701,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     __syncthreads();
     a_st = sm.a_stream[wave];
   };
-  // From the first current-chunk tile on, the int8 query operands are no longer needed;
+  // From the first current-chunk tile on, the cached keys' query operands are no longer needed;
   // their registers take the bf16 query (half h: channels HALF h .. HALF h + HALF - 1).
   auto load_query_bf16 = [&]() KVQ_INLINE {
     const uint4* qrow16 = reinterpret_cast<const uint4*>(p.q + ((size_t)bh * p.n_q + (q_ok ? qi : 0)) * D + HALF * h);

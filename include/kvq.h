@@ -174,11 +174,16 @@ typedef struct {
 } jb_attn_args;
 
 /* Corrected attention forward: writes o and, if given, mass_s/mass_r.
- * Numerics: with 2-bit per-token keys, cached-key scores take the rotated query as the
- * sum of three fp6 (e2m3) roundings (the query, then twice what is left), each with a
- * power-of-two scale per query and 32 channels, against the exact codes, summed in
- * fp32; with 4-bit or per-channel keys, the rotated query as a 16-bit fixed-point
- * integer (one scale per 32 queries) against the exact codes; softmax numerators are
+ * Numerics: with per-token keys, and with group-wise keys of 64 channels under the
+ * Taylor or no correction, cached-key scores take the rotated query as the sum of three
+ * fp6 (e2m3) roundings (the query, then twice what is left), each with a power-of-two
+ * scale per query and 32 channels, against the exact codes, summed in fp32 (4-bit keys
+ * with at most 32 queries: the rotated query as a 16-bit fixed-point integer, one scale
+ * per 32 queries, against the exact codes); with per-channel keys, the rotated query
+ * times the key group's steps as a 16-bit fixed-point integer (one scale per 32 queries
+ * and key group) against the exact codes; with group-wise keys of 32 channels, or
+ * group-wise keys under the exact correction, fp16 keys fp16((code - z) Delta) against
+ * the rotated query as fp16 hi + lo parts; softmax numerators are
  * fp16 (relative to a per-query reference max that is raised whenever a numerator could
  * leave the fp16 range), values fp16((code - z) Delta); sums and outputs fp32.
  * Preconditions on the data (not checked): key steps Delta < 2048 and |Delta z| < 65504

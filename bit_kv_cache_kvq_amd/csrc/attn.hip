@@ -427,6 +427,10 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // swap query channels so that K-step g holds group g), the codes as fp4 / fp6 rows, and
   // the logit sum_g (Delta_jg A) S_g + c with the groups' zero points in the bias.
   constexpr bool kF6G = TG == 64 && NG == 2 && !EXACT && !PERCH;
+  // 2-bit per-token keys issue each phase's first tile loads before the query build and
+  // before the switch to the current chunk (the other forms keep them in the pipeline
+  // start: their registers there would spill)
+  constexpr bool kPre = kF6 && BITS == 2;
   constexpr int KS6 = D / 64;  // fp6 K-steps of 64 channels (a lane holds 32 of each)
   constexpr int CBLK = D / 32;    // 32-channel output blocks
   constexpr int CPW = 32 / BITS;
@@ -727,7 +731,7 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
     }
     write_mslot();
   };
-  build_query();
+  if constexpr (!kPre) build_query();
 
   // ---------------- tile geometry ----------------
   const int tiles_per_chunk = p.cp / kBN;
@@ -1686,16 +1690,17 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   };
   // All tiles of one kind (tile U0 + T in slot T mod 3, the slots rotating with T): stage
   // the first two tiles' keys and the first values, then run the steps.
+  // (with kPre the caller has issued tile U0's key and value loads)
   auto run = [&](int U0, int n_t, auto k_c) KVQ_INLINE {
     const std::false_type no;
-    load_k(U0, k_c);
+    if constexpr (!kPre) load_k(U0, k_c);
     store_k(U0, 0, k_c);
     if (n_t > 1) {
       load_k(U0 + 1, k_c);
       store_k(U0 + 1, 1, k_c);
     }
     __syncthreads();
-    load_v(U0, k_c);
+    if constexpr (!kPre) load_v(U0, k_c);
     store_v(U0, 0, k_c);
     if (kEarlyK && n_t > 2) load_k(U0 + 2, k_c);
     if (kEarlyK && n_t > 1) load_v(U0 + 1, k_c);
@@ -1723,11 +1728,29 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   const int t_beg = cut(sp), t_end = cut(sp + 1);
   const int c_beg = min(t_beg, n_ct), c_end = min(t_end, n_ct);
   const int r_beg = max(t_beg, n_ct) - n_ct, r_end = max(t_end, n_ct) - n_ct;
+  // With kPre each phase's first tile is loaded before the work that precedes the phase
+  // (the query build, the un-rotation), whose instructions then cover the loads' latency.
+  if constexpr (kPre) {
+    if (c_end > c_beg) {
+      load_k(c_beg, Kind<kCached>());
+      load_v(c_beg, Kind<kCached>());
+    } else if (r_end > r_beg) {
+      load_k(n_ct + r_beg, Kind<kCurrent>());
+      load_v(n_ct + r_beg, Kind<kCurrent>());
+    }
+    build_query();
+  }
   if (c_end > c_beg) {
     if constexpr (PERCH) {
       if (computes) fill_qf();
     }
     run(c_beg, c_end - c_beg, Kind<kCached>());
+    if constexpr (kPre) {
+      if (r_end > r_beg) {
+        load_k(n_ct + r_beg, Kind<kCurrent>());
+        load_v(n_ct + r_beg, Kind<kCurrent>());
+      }
+    }
     if constexpr (!MASS_ONLY) {
       if (p.v_had && computes) unrotate();
     }

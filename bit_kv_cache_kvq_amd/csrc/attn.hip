@@ -427,10 +427,10 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
   // swap query channels so that K-step g holds group g), the codes as fp4 / fp6 rows, and
   // the logit sum_g (Delta_jg A) S_g + c with the groups' zero points in the bias.
   constexpr bool kF6G = TG == 64 && NG == 2 && !EXACT && !PERCH;
-  // 2-bit per-token keys issue each phase's first tile loads before the query build and
-  // before the switch to the current chunk (the other forms keep them in the pipeline
-  // start: their registers there would spill)
-  constexpr bool kPre = kF6 && BITS == 2;
+  // 2-bit per-token keys (Taylor or no correction) issue each phase's first tile loads
+  // before the query build and before the switch to the current chunk (the other forms
+  // keep them in the pipeline start: measured slower, or their registers there spill)
+  constexpr bool kPre = kF6 && BITS == 2 && !EXACT;
   constexpr int KS6 = D / 64;  // fp6 K-steps of 64 channels (a lane holds 32 of each)
   constexpr int CBLK = D / 32;    // 32-channel output blocks
   constexpr int CPW = 32 / BITS;

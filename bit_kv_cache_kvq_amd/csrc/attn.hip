@@ -229,8 +229,7 @@ struct SmemSlots {
   struct PSlot {
     float dka[kNS][kBN];  // Delta_j A of each stream (cached; 0 for padding), M-row order
     uint4 kb[kBN][2];     // bias operand rows (16 fp16), M-row order
-    float d2[kBN];        // exact correction, per-token keys: Delta_j^2 and Delta_j^4, M-row order
-    float d4[kBN];
+    float spare[2 * kBN];  // unused; without it c40 measured 2% slower (LDS placement)
   };
   struct ZSlot {
     uint32_t zv[kBN / 2];   // (-1024 - z^V) fp16 pairs, token pair (j, j+8) order
@@ -661,6 +660,25 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
 #pragma unroll
       for (int e = 3; e < 8; e++) qbias[e] = (_Float16)0.f;
     }
+    if constexpr (EXACT && !PERCH && TG == 0) {
+      // the exact correction's terms past the second order, e2 D^4 - e3 D^6 + e4 D^8, ride
+      // on the free bias slots against the key powers u^2, u^3, u^4 of u = D^2 / 64:
+      // D^4 as (hi, lo, hi) in slots 6, 7, 11, D^6 likewise in 12, 13, 14, D^8 in 15
+      _Float16 a4h, a4l, a6h, a6l;
+      split16(fminf(ex2 * 4096.f, 65504.f), a4h, a4l);
+      split16(fmaxf(-ex3 * 262144.f, -65504.f), a6h, a6l);
+      const _Float16 a8 = (_Float16)fminf(ex4 * 16777216.f, 65504.f);
+      if (h == 0) {
+        qbias[6] = a4h;
+        qbias[7] = a4l;
+      } else {
+        qbias[3] = a4h;
+        qbias[4] = a6h;
+        qbias[5] = a6l;
+        qbias[6] = a6h;
+        qbias[7] = a8;
+      }
+    }
     if constexpr (TG > 0) {
       // term t: the correction of group t, -s^2 |q'_t|^2 / 24 (times 64, log2 units); its
       // three slots are k = 3t .. 3t+2 at bias slot k + 3 (k >= 8): 8, 9, 10 carry -m and
@@ -1077,10 +1095,6 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         const int r = 32 * (key >> 5) + key_mrow(key & 31);
         const float dk = key < nv ? half_bits_to_f32(pk_dk) : 0.f;
         ps.dka[wave][r] = dk * a_st;
-        if (EXACT && !PERCH && wave == 3) {
-          ps.d2[r] = dk * dk;
-          ps.d4[r] = (dk * dk) * (dk * dk);
-        }
       }
       if constexpr (TG > 0) {
         if (wave == 0) {
@@ -1142,8 +1156,37 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
           row.x = dzh_b | (dzh_b << 16);
           row.y = dzl_b | (d2h_b << 16);
           row.z = d2h_b | (d2l_b << 16);
+          if constexpr (EXACT) {
+            const float u = dk * dk * (1.f / kD2Scale);
+            _Float16 u4h, u4l;
+            split16(fminf(u * u, 65504.f), u4h, u4l);
+            const uint32_t u4h_b = __builtin_bit_cast(uint16_t, u4h);
+            row.w = u4h_b | (u4h_b << 16);
+          }
         }
         ps.kb[r][0] = row;
+      }
+      if constexpr (EXACT && TG == 0 && !PERCH) {
+        if (wave == 1) {
+          // slots 8..15: 1, 1, the mask, then the D^4 lo part, D^6 (hi, hi, lo), D^8
+          const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
+          const uint32_t one = 0x3C00u;
+          uint4 row = make_uint4(one | (one << 16), one, 0u, 0u);
+          if (lane < nv) {
+            const float dk = half_bits_to_f32(pk_dk);
+            const float u = dk * dk * (1.f / kD2Scale), u2 = u * u;
+            _Float16 u4h, u4l, u6h, u6l;
+            split16(fminf(u2, 65504.f), u4h, u4l);
+            split16(fminf(u2 * u, 65504.f), u6h, u6l);
+            const _Float16 u8 = (_Float16)fminf(u2 * u2, 65504.f);
+            const uint32_t u4l_b = __builtin_bit_cast(uint16_t, u4l), u6h_b = __builtin_bit_cast(uint16_t, u6h);
+            const uint32_t u6l_b = __builtin_bit_cast(uint16_t, u6l), u8_b = __builtin_bit_cast(uint16_t, u8);
+            row.y = u4l_b << 16;
+            row.z = u6h_b | (u6h_b << 16);
+            row.w = u6l_b | (u8_b << 16);
+          }
+          ps.kb[r][1] = row;
+        }
       }
       if constexpr (!MASS_ONLY && TG > 0) {
         if (wave == 2 && lane < kBN / 2) {
@@ -1181,7 +1224,8 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         ps.kb[r][0] = make_uint4(0, 0, 0, 0);
       }
     }
-    if (wave == 1 && !(TG > 0 && decltype(k_c)::value == kCached)) {
+    if (wave == 1 && !(TG > 0 && decltype(k_c)::value == kCached) &&
+        !(EXACT && TG == 0 && !PERCH && decltype(k_c)::value == kCached)) {
       // bias key operand, slots 8..15: 1, 1, mask, 0...
       const int r = 32 * (lane >> 5) + key_mrow(lane & 31);
       const uint32_t one = 0x3C00u;
@@ -1500,19 +1544,6 @@ __device__ KVQ_INLINE void attn_body(const Params p, const int wg, const int n_w
         for (int b = 0; b < 4; b++) {
           const int v = 4 * v4 + b;
           x[v] = fmaf(d[b], kF6 ? __int_as_float(sqh[SET][v]) : (float)sqh[SET][v], cb[SET][v]);
-        }
-        if constexpr (EXACT && !PERCH) {
-          // the exact correction's terms past the second order: -b gains
-          // Delta^4 (c2 M2 - Delta^2 (c3 M3 - Delta^2 c4 M4))
-          const float4 e2v = *reinterpret_cast<const float4*>(&sm.prm[slot].d2[32 * mb + 8 * v4 + 4 * h]);
-          const float4 e4v = *reinterpret_cast<const float4*>(&sm.prm[slot].d4[32 * mb + 8 * v4 + 4 * h]);
-          const float dd2[4] = {e2v.x, e2v.y, e2v.z, e2v.w}, dd4[4] = {e4v.x, e4v.y, e4v.z, e4v.w};
-#pragma unroll
-          for (int b = 0; b < 4; b++) {
-            const int v = 4 * v4 + b;
-            const float t = fmaf(-dd2[b], fmaf(-dd2[b], ex4, ex3), ex2);
-            x[v] = fmaf(dd4[b], t, x[v]);
-          }
         }
       }
     } else {

@@ -199,14 +199,17 @@ EDGES = [
 
 @pytest.mark.parametrize("shape", EDGES, ids=lambda s: "x".join(str(v) for v in s.values()))
 @pytest.mark.parametrize("bits", [2, 4])
-def test_edges_all_rows(shape, bits):
+@pytest.mark.parametrize("correction", [1, 2])
+def test_edges_all_rows(shape, bits, correction):
+    """Ragged shapes under the Taylor and the exact correction (the exact one's terms share
+    the bias operand with the padding mask)."""
     w = synth.Workload("edge", **shape, bits=bits, seed=3)
-    print(f"attn edge {shape} bits={bits}", flush=True)
+    print(f"attn edge {shape} bits={bits} correction={correction}", flush=True)
     x = synth.draw_all(w)
-    O, PS, PR = run_gpu(x, w)
-    Or, PSr, PRr = run_oracle(x, w)
-    assert_attention_close(O, Or, f"edge {shape}")
-    assert_mass_close(PS, PR, PSr, PRr, f"edge {shape}")
+    O, PS, PR = run_gpu(x, w, correction=correction)
+    Or, PSr, PRr = run_oracle(x, w, correction={1: "taylor", 2: "exact"}[correction])
+    assert_attention_close(O, Or, f"edge {shape} c{correction}")
+    assert_mass_close(PS, PR, PSr, PRr, f"edge {shape} c{correction}")
 
 
 # per-channel keys (one step pair per channel over a token group): groups of 64 and 128,
@@ -389,6 +392,21 @@ def test_split_window_matches_unsplit(name):
     _, PS2, PR2 = run_gpu(x, w, mass_only=True, split=True)
     np.testing.assert_allclose(PS2, a[1], atol=2e-6)
     np.testing.assert_allclose(PR2, a[2], atol=2e-6)
+
+
+@pytest.mark.parametrize("name", ["mix1", "mix3"])
+def test_split_window_exact_correction(name):
+    """The ragged split shapes under the exact correction (its kernels start each phase's
+    pipeline themselves), split and unsplit, against the oracle on every row."""
+    w = SPLIT_MIX[name]
+    x = synth.draw_all(w)
+    print(f"attn split exact {name}", flush=True)
+    Or, PSr, PRr = run_oracle(x, w, correction="exact")
+    for split in (True, False):
+        O, PS, PR = run_gpu(x, w, split=split, correction=2)
+        assert (run_gpu.last_workspace_bytes > 0) == split
+        assert_attention_close(O, Or, f"split exact {name} split={split}")
+        assert_mass_close(PS, PR, PSr, PRr, f"split exact {name} split={split}")
 
 
 def test_deterministic():

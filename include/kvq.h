@@ -139,8 +139,9 @@ int kvq_pack(const uint16_t* x, int32_t B, int32_t H, int32_t n, int32_t d, cons
  * channel's term below 1e-6). Per-token keys evaluate its power series in Delta_j through
  * Delta_j^8 (the omitted terms are below (max_c x)^8 sum_c x^2 / 467775 nats: 2e-6 per
  * channel at x = 1; the series does not converge past x = pi; its terms past the second
- * order are products of fp16 hi/lo pairs whose key-side powers of Delta_j saturate from
- * Delta_j = 32 on, where x passes pi for every channel with s |q'_ic| > 0.2); group-wise
+ * order are fp16 products (hi/lo pairs for the Delta^4 and Delta^6 terms) whose key-side
+ * powers of Delta_j saturate from Delta_j = 32 on, where x passes pi for every channel
+ * with s |q'_ic| > 0.2); group-wise
  * per-token keys the same series per channel group, in that group's step Delta_j,grp. */
 typedef struct {
   int32_t B, H, d;            /* d in {64, 128}; the same H for queries and keys */
